@@ -1,0 +1,105 @@
+"""CPU oracle for the channels-last convolution forward pass -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it, and the two share no code.
+
+The arithmetic lives in ``conv_oracle.c`` (a direct loop nest over every
+output, every tap and every input channel, accumulated in float64; see the
+header of that file for the definition and the pages it follows).  This module
+only marshals numpy arrays into it and decodes fp16/bf16/fp32 tensors to
+float64, which is exact for all three formats.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "n", "d", "h", "w", "c_in", "c_out",
+        "k_d", "k_h", "k_w", "s_d", "s_h", "s_w", "p_d", "p_h", "p_w")]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        # ORACLE_CONV_LIB points the wrapper at another build of conv_oracle.c; the
+        # mutation tests use it to load copies with planted mistakes.
+        path = os.environ.get("ORACLE_CONV_LIB", _build.LIB)
+        if path == _build.LIB and not os.path.exists(path):
+            _build.build()
+        lib = ctypes.CDLL(path)
+        lib.oracle_conv_fwd.restype = ctypes.c_int64
+        lib.oracle_conv_fwd.argtypes = [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.oracle_out_extent.restype = ctypes.c_int64
+        lib.oracle_out_extent.argtypes = [ctypes.c_int64] * 4
+        _lib = lib
+    return _lib
+
+
+def _triple(v, dims):
+    if isinstance(v, int):
+        return (v,) * dims
+    v = tuple(int(e) for e in v)
+    assert len(v) == dims
+    return v
+
+
+def out_extent(size: int, k: int, s: int, p: int) -> int:
+    """floor((size + 2p - k) / s) + 1, or 0 if the padded input is shorter than k."""
+    return int(_load().oracle_out_extent(size, k, s, p))
+
+
+def conv_fwd(x: np.ndarray, w: np.ndarray, stride=1, padding=0, rows=None,
+             return_macs: bool = False):
+    """Direct convolution, float64.
+
+    x: (N, H, W, C_in) or (N, D, H, W, C_in); w: (C_out, KH, KW, C_in) or
+    (C_out, KD, KH, KW, C_in); stride and padding: int or per-dimension tuple.
+    Returns y with shape (N, [D_out,] H_out, W_out, C_out), or, when ``rows``
+    (flat output-position indices) is given, an array (len(rows), C_out).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    dims = x.ndim - 2
+    assert dims in (2, 3) and w.ndim == x.ndim and w.shape[-1] == x.shape[-1]
+    st = _triple(stride, dims)
+    pd = _triple(padding, dims)
+    if dims == 2:
+        x5 = x.reshape(x.shape[0], 1, *x.shape[1:])
+        w5 = w.reshape(w.shape[0], 1, *w.shape[1:])
+        st, pd = (1,) + st, (0,) + pd
+    else:
+        x5, w5 = x, w
+    sh = _Shape(x5.shape[0], x5.shape[1], x5.shape[2], x5.shape[3], x5.shape[4], w5.shape[0],
+                w5.shape[1], w5.shape[2], w5.shape[3], *st, *pd)
+    outs = [out_extent(x5.shape[1 + i], w5.shape[1 + i], st[i], pd[i]) for i in range(3)]
+    if rows is None:
+        y = np.zeros((x5.shape[0], *outs, w5.shape[0]), dtype=np.float64)
+        rows_ptr, nrows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        y = np.zeros((rows.shape[0], w5.shape[0]), dtype=np.float64)
+        rows_ptr, nrows = rows.ctypes.data, rows.shape[0]
+    macs = _load().oracle_conv_fwd(ctypes.byref(sh), x5.ctypes.data, w5.ctypes.data,
+                                   rows_ptr, nrows, y.ctypes.data)
+    if macs < 0:
+        raise ValueError("oracle rejected the shape or a row index")
+    if rows is None and dims == 2:
+        y = y.reshape(y.shape[0], *y.shape[2:])
+    return (y, int(macs)) if return_macs else y
+
+
+def to_float64(t) -> np.ndarray:
+    """Exact float64 copy of a CPU or GPU fp16 / bf16 / fp32 tensor (or ndarray)."""
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
+    import torch
+    return t.detach().to("cpu").to(dtype=torch.float64).numpy()

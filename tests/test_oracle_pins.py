@@ -1,0 +1,256 @@
+"""Pins the CPU oracle to facts the pages and the mathematics fix (no GPU needed).
+
+Each test names what it pins.  Together they are chosen so that a plausible
+slip in the oracle (a flipped kernel, a wrong sign or offset in the padding,
+a stride applied to the wrong term, a transposed weight index, a dropped
+channel or tap, a ceil instead of a floor) fails at least one of them; the
+mutation tests in test_oracle_mutants.py plant such slips and check that.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.im2col_ref import conv_im2col
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _read_matrices(path):
+    mats, cur, name = {}, None, None
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        parts = line.split()
+        if parts[0].isalpha():
+            name = parts[0]
+            cur = mats[name] = []
+        else:
+            cur.append([float(v) for v in parts])
+    return {k: np.array(v) for k, v in mats.items()}
+
+
+def _rows(path):
+    out = []
+    for line in open(path):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            out.append(line.split())
+    return out
+
+
+# --- the pages' worked example -------------------------------------------------
+
+def test_worked_example_2x2_on_3x3():
+    """"Convolutions" section 4: [[1,2,3],[4,5,6],[7,8,9]] with [[1,0],[0,-1]] -> [[-4,-4],[-4,-4]]."""
+    g = _read_matrices(os.path.join(GOLDEN, "worked_example_2x2_on_3x3.txt"))
+    x = g["input"].reshape(1, 3, 3, 1)
+    k = g["kernel"].reshape(1, 2, 2, 1)
+    y = oracle.conv_fwd(x, k)
+    assert y.shape == (1, 2, 2, 1)
+    np.testing.assert_array_equal(y[0, :, :, 0], g["output"])
+    # The flipped (true convolution) orientation gives +4 everywhere: the example
+    # decides the orientation, so the oracle must not match the flipped kernel.
+    y_flip = oracle.conv_fwd(x, k[:, ::-1, ::-1, :].copy())
+    assert np.all(y_flip[0, :, :, 0] == 4.0)
+
+
+def test_flop_formula_counts():
+    """"Convolutions" sections 4 and 5: the oracle performs exactly the multiply-adds the FLOP
+    formula 2*H_out*W_out*C_in*C_out*K_h*K_w counts, for the printed 236 MFLOPs and 3.7 GFLOP."""
+    for name, h, w, cin, cout, k, s, p, printed, unit, digits in _rows(
+            os.path.join(GOLDEN, "flop_counts.txt")):
+        h, w, cin, cout, k, s, p, digits = map(int, (h, w, cin, cout, k, s, p, digits))
+        x = np.zeros((1, h, w, cin))
+        wt = np.zeros((cout, k, k, cin))
+        y, macs = oracle.conv_fwd(x, wt, stride=s, padding=p, return_macs=True)
+        scale = {"MFLOP": 1e6, "GFLOP": 1e9}[unit]
+        assert round(2 * macs / scale, digits) == float(printed), name
+        ho, wo = y.shape[1], y.shape[2]
+        assert 2 * macs == 2 * ho * wo * cin * cout * k * k, name
+
+
+def test_output_extents():
+    """Output extents printed or implied by the pages (floor reading)."""
+    for i, k, s, p, expected, *_ in _rows(os.path.join(GOLDEN, "output_extents.txt")):
+        assert oracle.out_extent(int(i), int(k), int(s), int(p)) == int(expected)
+    # and the oracle's output array has those extents (stem layer and the stride-2 3D row)
+    y = oracle.conv_fwd(np.zeros((1, 224, 224, 3)), np.zeros((1, 7, 7, 3)), 2, 3)
+    assert y.shape == (1, 112, 112, 1)
+    y = oracle.conv_fwd(np.zeros((1, 32, 32, 32, 1)), np.zeros((1, 3, 3, 3, 1)), 2, 1)
+    assert y.shape == (1, 16, 16, 16, 1)
+
+
+def test_memory_column_matches_floor_extent():
+    """MLX PR fp16 table: the implicit path's peak memory equals |x|+|w|+|y| in MiB.
+    For the stride-2 row (4,32^3,64) -> 128 it prints 20.4, which only the floor
+    extent (16^3 outputs) reproduces; the ceil extent (17^3) would give 21.2."""
+    def mib(n_elems):
+        return n_elems * 2 / 2**20
+    od = oracle.out_extent(32, 3, 2, 1)
+    total = mib(4 * 32**3 * 64) + mib(128 * 27 * 64) + mib(4 * od**3 * 128)
+    assert round(total, 1) == 20.4
+    # the unit-stride rows of the same table: (4,32^3,128->128) printed 64.8
+    od = oracle.out_extent(32, 3, 1, 1)
+    assert round(mib(4 * 32**3 * 128) + mib(128 * 27 * 128) + mib(4 * od**3 * 128), 1) == 64.8
+
+
+# --- closed forms ----------------------------------------------------------------
+
+def _valid_taps_1d(size, k, s, p, o):
+    """Number of filter offsets t in [0, k) with 0 <= o*s - p + t < size (interval count)."""
+    lo = max(0, p - o * s)
+    hi = min(k, size + p - o * s)
+    return max(0, hi - lo)
+
+
+TAP_SHAPES = [
+    # (D, H, W), (KD, KH, KW), stride, pad
+    ((5, 6, 7), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
+    ((4, 5, 9), (3, 2, 3), (2, 1, 3), (1, 0, 2)),
+    ((3, 7, 6), (1, 3, 5), (1, 2, 2), (0, 1, 2)),
+    ((6, 4, 5), (3, 3, 3), (3, 3, 2), (3, 2, 3)),     # pad larger than k-1: all-padding windows
+    ((1, 11, 12), (1, 7, 7), (1, 2, 2), (0, 3, 3)),   # stem-like 2D
+    ((4, 4, 4), (3, 1, 1), (1, 1, 1), (1, 0, 0)),
+    ((4, 4, 4), (1, 3, 3), (1, 1, 1), (0, 1, 1)),
+]
+
+
+@pytest.mark.parametrize("spatial,ks,st,pd", TAP_SHAPES)
+def test_tap_count_closed_form(spatial, ks, st, pd):
+    """x = 1 everywhere and w = 1 only on input channel 0: each output counts the
+    in-bounds taps of its window, a product of per-dimension interval lengths."""
+    n, cin, cout = 2, 3, 2
+    x = np.ones((n, *spatial, cin))
+    w = np.zeros((cout, *ks, cin))
+    w[..., 0] = 1.0
+    y = oracle.conv_fwd(x, w, st, pd)
+    outs = [oracle.out_extent(spatial[i], ks[i], st[i], pd[i]) for i in range(3)]
+    assert y.shape == (n, *outs, cout)
+    for od in range(outs[0]):
+        for oh in range(outs[1]):
+            for ow in range(outs[2]):
+                expect = (_valid_taps_1d(spatial[0], ks[0], st[0], pd[0], od)
+                          * _valid_taps_1d(spatial[1], ks[1], st[1], pd[1], oh)
+                          * _valid_taps_1d(spatial[2], ks[2], st[2], pd[2], ow))
+                assert np.all(y[:, od, oh, ow, :] == expect)
+
+
+GATHER_CASES = [((5, 6, 7), (3, 3, 3), (s, s, s), (p, p, p)) for s in (1, 2, 3) for p in (0, 1, 2, 3)]
+
+
+@pytest.mark.parametrize("spatial,ks,st,pd", GATHER_CASES)
+def test_one_hot_gather(spatial, ks, st, pd):
+    """w = delta at one tap (kd*, kh*, kw*) with c_out = c_in: the output is the input
+    shifted by that tap and subsampled by the stride, zero where it falls in the padding.
+    Checked for every tap against numpy pad + strided slicing."""
+    if any(oracle.out_extent(spatial[i], ks[i], st[i], pd[i]) < 1 for i in range(3)):
+        pytest.skip("empty output")
+    rng = np.random.default_rng(7)
+    n, c = 2, 3
+    x = rng.integers(-50, 50, size=(n, *spatial, c)).astype(np.float64)
+    outs = [oracle.out_extent(spatial[i], ks[i], st[i], pd[i]) for i in range(3)]
+    big = 16
+    xp = np.pad(x, ((0, 0), (pd[0], big), (pd[1], big), (pd[2], big), (0, 0)))
+    for a in range(ks[0]):
+        for b in range(ks[1]):
+            for e in range(ks[2]):
+                w = np.zeros((c, *ks, c))
+                for ch in range(c):
+                    w[ch, a, b, e, ch] = 1.0
+                y = oracle.conv_fwd(x, w, st, pd)
+                expect = xp[:, a:a + outs[0] * st[0]:st[0], b:b + outs[1] * st[1]:st[1],
+                            e:e + outs[2] * st[2]:st[2], :]
+                np.testing.assert_array_equal(y, expect)
+
+
+def test_pointwise_is_matmul():
+    """"Convolutions" section 5, variants: a 1x1 stride-1 unpadded convolution is a GEMM
+    over channels: y[M, C_out] = X[M, C_in] @ W^T."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((2, 3, 5, 6, 7))
+    w = rng.standard_normal((4, 1, 1, 1, 7))
+    y = oracle.conv_fwd(x, w, 1, 0)
+    ref = np.matmul(x.reshape(-1, 7), w.reshape(4, 7).T).reshape(2, 3, 5, 6, 4)
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_linearity():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 4, 5, 6, 3))
+    w1 = rng.standard_normal((5, 3, 2, 3, 3))
+    w2 = rng.standard_normal((5, 3, 2, 3, 3))
+    st, pd = (2, 1, 2), (1, 0, 2)
+    y1 = oracle.conv_fwd(x, w1, st, pd)
+    y2 = oracle.conv_fwd(x, w2, st, pd)
+    np.testing.assert_allclose(oracle.conv_fwd(x, w1 + w2, st, pd), y1 + y2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle.conv_fwd(3.0 * x, w1, st, pd), 3.0 * y1, rtol=1e-12, atol=1e-12)
+
+
+# --- independent brute force ---------------------------------------------------------
+
+def _random_case(rng):
+    dims = int(rng.integers(2, 4))
+    n = int(rng.integers(1, 3))
+    cin = int(rng.choice([1, 2, 3, 5, 8]))
+    cout = int(rng.integers(1, 6))
+    ks = [int(rng.integers(1, 4)) for _ in range(3)]
+    st = [int(rng.integers(1, 4)) for _ in range(3)]
+    pd = [int(rng.integers(0, 4)) for _ in range(3)]
+    sp = [int(rng.integers(1, 8)) for _ in range(3)]
+    if dims == 2:
+        ks[0], st[0], pd[0], sp[0] = 1, 1, 0, 1
+    for i in range(3):                     # keep at least one output along each dimension
+        while sp[i] + 2 * pd[i] < ks[i]:
+            sp[i] += 1
+    return n, cin, cout, sp, ks, st, pd
+
+
+def test_matches_im2col_on_random_tiny_shapes():
+    """Exercise A of the tutorial: the direct loop nest equals im2col + GEMM, on 250
+    random tiny 2D and 3D shapes (strides 1-3, pads 0-3, odd and unit channel counts)."""
+    rng = np.random.default_rng(2024)
+    for case in range(250):
+        n, cin, cout, sp, ks, st, pd = _random_case(rng)
+        x = rng.standard_normal((n, *sp, cin))
+        w = rng.standard_normal((cout, *ks, cin))
+        y = oracle.conv_fwd(x, w, st, pd)
+        ref = conv_im2col(x, w, st, pd)
+        assert y.shape == ref.shape, (case, sp, ks, st, pd)
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12, err_msg=str(case))
+
+
+def test_rows_subset_equals_full():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((2, 5, 6, 7, 4))
+    w = rng.standard_normal((3, 3, 3, 3, 4))
+    full = oracle.conv_fwd(x, w, (1, 2, 1), (1, 1, 0))
+    flat = full.reshape(-1, 3)
+    rows = np.array([0, 5, flat.shape[0] - 1, 17, 17])
+    np.testing.assert_array_equal(oracle.conv_fwd(x, w, (1, 2, 1), (1, 1, 0), rows=rows), flat[rows])
+    with pytest.raises(ValueError):
+        oracle.conv_fwd(x, w, (1, 2, 1), (1, 1, 0), rows=np.array([flat.shape[0]]))
+
+
+def test_empty_batch():
+    y = oracle.conv_fwd(np.zeros((0, 4, 4, 4, 2)), np.zeros((3, 3, 3, 3, 2)), 1, 1)
+    assert y.shape == (0, 4, 4, 4, 3)
+
+
+# --- exact decoding of the input formats --------------------------------------------
+
+def test_decode_formats_exactly():
+    """fp16 / bf16 / fp32 to float64 is exact, subnormals included."""
+    f16 = torch.tensor([0x3C00, 0x0001, 0x7BFF, 0x8400, 0x3555], dtype=torch.int32).to(torch.int16)
+    f16 = f16.view(torch.float16)
+    np.testing.assert_array_equal(oracle.to_float64(f16),
+                                  [1.0, 2.0**-24, 65504.0, -2.0**-14, 0.333251953125])
+    bf = torch.tensor([0x3F80, 0x0001, 0x7F7F, 0xC000], dtype=torch.int32).to(torch.int16)
+    bf = bf.view(torch.bfloat16)
+    np.testing.assert_array_equal(oracle.to_float64(bf),
+                                  [1.0, 2.0**-133, (2 - 2.0**-7) * 2.0**127, -2.0])
+    f32 = torch.tensor([1.0 + 2.0**-23, 2.0**-149], dtype=torch.float32)
+    np.testing.assert_array_equal(oracle.to_float64(f32), [1.0 + 2.0**-23, 2.0**-149])
