@@ -1,0 +1,161 @@
+"""Throughput of the channels-last implicit-GEMM convolution forward on one MI355X.
+
+A step is one pass over the fp16 3x3x3 NDHWC sweep
+  (4,32^3,128->128, s1 p1), (1,64^3,64->128, s1 p1), (4,32^3,64->128, s2 p1)
+with seeded synthetic inputs already resident in HBM; each convolution is one
+launch of the library's auto path on the current stream.  The metric is
+2*M*N*K FLOPs (M = output positions, N = C_out, K = C_in*27) per second over
+the timed steps, in TFLOP/s.
+
+The JSON line also carries
+  roofline:     the dominant kernel (the one running the two 116-GFLOP
+                convolutions) timed launch by launch with HIP events on the
+                launch stream, against the MI355X dense fp16 MFMA peak;
+  cpu_baseline: the float64 CPU oracle on a bounded sample of the same
+                workload (a fixed set of output rows of the first convolution),
+                on this host's cores, rank 0 only.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import implicit_gemm_conv_amd as igc  # noqa: E402
+from conv_workloads import HEADLINE, WORKLOADS, make_inputs  # noqa: E402
+
+PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}   # MI355X dense, published
+METRIC = "conv fwd TFLOP/s (2·M·N·K) and % of MFMA peak, fp16 NDHWC 3×3×3 shapes"
+
+
+def gemm_dims(wl):
+    out = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding)
+    m = int(np.prod(out[:-1]))
+    n = wl.w_shape[0]
+    k = int(np.prod(wl.w_shape[1:]))
+    return m, n, k
+
+
+def kernel_key(wl):
+    """Kernels are identified by path + tile choice; the two unit-stride 116-GFLOP
+    convolutions share one kernel instantiation."""
+    return igc.select_path(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.torch_dtype)
+
+
+def cpu_baseline(wl, x, w, rows_count=4096):
+    import oracle
+    xf = oracle.to_float64(x)
+    wf = oracle.to_float64(w)
+    m, n, k = gemm_dims(wl)
+    rows = np.linspace(0, m - 1, rows_count).astype(np.int64)
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    oracle.conv_fwd(xf, wf, wl.stride, wl.padding, rows=rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows_count * n * k
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{wl.name}: {rows_count} of {m} output rows (evenly spaced), all {n} "
+                      f"channels, float64 direct loop; {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=65536)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the convolution would shard by batch or C_out with no exchange).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wls = [WORKLOADS[n] for n in HEADLINE]
+    inputs = [make_inputs(wl, dev) for wl in wls]
+    outs = [torch.empty(igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding),
+                        dtype=wl.torch_dtype, device=dev) for wl in wls]
+    dims = [gemm_dims(wl) for wl in wls]
+    flops = [2.0 * m * n * k for (m, n, k) in dims]
+    step_flops = sum(flops)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for i, wl in enumerate(wls):
+            x, w = inputs[i]
+            if events is not None:
+                events[i][0].record(stream)
+            igc.conv_fwd(x, w, wl.stride, wl.padding, out=outs[i])
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps between two synchronisations.
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in wls] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(ev[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    per = {}
+    for i, wl in enumerate(wls):
+        times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        us = 1e3 * float(np.mean(times))
+        per[wl.name] = {"path": kernel_key(wl), "us_mean": round(us, 3),
+                        "us_min": round(1e3 * float(np.min(times)), 3),
+                        "tflops": round(flops[i] / (us * 1e-6) / 1e12, 2),
+                        "pct_peak": round(100 * flops[i] / (us * 1e-6) / 1e12 / PEAK_TFLOPS["fp16"], 2)}
+
+    # Dominant kernel: the one running the two unit-stride 116-GFLOP convolutions.
+    dom = [0, 1]
+    dom_us = float(np.mean([1e3 * ev[s][i][0].elapsed_time(ev[s][i][1])
+                            for s in range(args.steps) for i in dom]))
+    dom_flops = flops[0]
+    achieved = dom_flops / (dom_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp16"],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp16"], 4),
+                "traffic": None,
+                "kernel": "conv_main_kernel<fp16, BM=256, BN=128> (c4a, c4b)",
+                "launch_us": round(dom_us, 3), "flops_per_launch": dom_flops}
+
+    value = step_flops * args.steps / (total_ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded x ~ U[-1,1), w ~ N(0,1)/sqrt(fan_in), fp16)",
+        "config": {"workload": "conv3d fwd fp16 NDHWC 3x3x3 pad 1 sweep: "
+                               "(4,32^3,128->128,s1), (1,64^3,64->128,s1), (4,32^3,64->128,s2)",
+                   "gemm_mnk": dims, "gflop_per_step": round(step_flops / 1e9, 3)},
+        "per_workload": per,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        x0, w0 = inputs[0]
+        rec["cpu_baseline"] = cpu_baseline(wls[0], x0, w0, args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

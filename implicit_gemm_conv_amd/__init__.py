@@ -1,0 +1,148 @@
+"""Python binding of libconvfwd.so, the gfx950 channels-last implicit-GEMM convolution.
+
+Argument marshalling only: every step of the convolution runs in the HIP
+kernels behind the C ABI of include/convfwd.h.  PyTorch provides device
+memory and the stream.  There is no CPU fallback: if the library is missing
+or the tensors are not on a GPU, the call raises.
+
+    import implicit_gemm_conv_amd as igc
+    y = igc.conv_fwd(x, w, stride=1, padding=1)        # x (N,[D,]H,W,C), w (Co,[KD,]KH,KW,C)
+"""
+import ctypes
+import os
+
+import torch
+
+from .build import LIB as _LIB_PATH
+
+PATHS = {"auto": 0, "main": 1, "flatk": 2, "rows": 3, "direct": 4}
+PATH_NAMES = {v: k for k, v in PATHS.items()}
+_DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+class ConvError(RuntimeError):
+    """A non-zero return code from the C ABI."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"convfwd error {code}: {msg}")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    """Mirror of convfwd_desc."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "n", "d", "h", "w", "c_in", "c_out", "k_d", "k_h", "k_w",
+        "s_d", "s_h", "s_w", "p_d", "p_h", "p_w", "groups", "dtype")]
+
+
+# Every entry point the header declares: (name, restype, argtypes).
+EXPORTS = [
+    ("conv_out_shape", ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_int64)]),
+    ("conv_select_path", ctypes.c_int, [ctypes.POINTER(Desc)]),
+    ("conv_fwd", ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_void_p, ctypes.c_void_p]),
+    ("conv_fwd_path", ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("conv_strerror", ctypes.c_char_p, [ctypes.c_int]),
+    ("conv_path_name", ctypes.c_char_p, [ctypes.c_int]),
+]
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                              "`python -m implicit_gemm_conv_amd.build`")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, res, args in EXPORTS:
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(code: int) -> int:
+    if code < 0:
+        raise ConvError(code, lib().conv_strerror(code).decode())
+    return code
+
+
+def _triple(v, dims, what):
+    if isinstance(v, int):
+        v = (v,) * dims
+    v = tuple(int(e) for e in v)
+    if len(v) != dims:
+        raise ValueError(f"{what} needs {dims} entries, got {v}")
+    return v
+
+
+def make_desc(x_shape, w_shape, stride=1, padding=0, dtype=torch.float16, groups=1) -> Desc:
+    """Descriptor for x (N,[D,]H,W,C_in) and w (C_out,[KD,]KH,KW,C_in) shapes."""
+    dims = len(x_shape) - 2
+    if dims not in (2, 3) or len(w_shape) != len(x_shape):
+        raise ValueError(f"expected 4-D (2D) or 5-D (3D) x and w, got {x_shape}, {w_shape}")
+    st = _triple(stride, dims, "stride")
+    pd = _triple(padding, dims, "padding")
+    if dims == 2:
+        x_shape = (x_shape[0], 1, *x_shape[1:])
+        w_shape = (w_shape[0], 1, *w_shape[1:])
+        st, pd = (1, *st), (0, *pd)
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return Desc(x_shape[0], x_shape[1], x_shape[2], x_shape[3], x_shape[4], w_shape[0],
+                w_shape[1], w_shape[2], w_shape[3], *st, *pd, groups, _DTYPES[dtype])
+
+
+def out_shape(x_shape, w_shape, stride=1, padding=0):
+    """Output shape (N,[D_out,]H_out,W_out,C_out) as the library computes it."""
+    d = make_desc(x_shape, w_shape, stride, padding)
+    out = (ctypes.c_int64 * 5)()
+    _check(lib().conv_out_shape(ctypes.byref(d), out))
+    shape = tuple(int(v) for v in out)
+    return shape if len(x_shape) == 5 else (shape[0], *shape[2:])
+
+
+def select_path(x_shape, w_shape, stride=1, padding=0, dtype=torch.float16) -> str:
+    """Name of the path the library picks for this problem."""
+    d = make_desc(x_shape, w_shape, stride, padding, dtype)
+    return PATH_NAMES[_check(lib().conv_select_path(ctypes.byref(d)))]
+
+
+def conv_fwd(x: torch.Tensor, w: torch.Tensor, stride=1, padding=0, out: torch.Tensor = None,
+             path: str = "auto") -> torch.Tensor:
+    """Channels-last convolution forward on the GPU.
+
+    x: (N,H,W,C_in) or (N,D,H,W,C_in); w: (C_out,KH,KW,C_in) or (C_out,KD,KH,KW,C_in);
+    same dtype (fp32, fp16 or bf16), same CUDA/HIP device.  Non-contiguous
+    inputs are made contiguous first.  Returns y (N,[D_out,]H_out,W_out,C_out)
+    in x's dtype, launched on the current stream of x's device (not synchronised).
+    """
+    if not (x.is_cuda and w.is_cuda):
+        raise ValueError("conv_fwd runs on the GPU only: x and w must be device tensors")
+    if x.device != w.device or x.dtype != w.dtype:
+        raise ValueError("x and w must share device and dtype")
+    x = x.contiguous()
+    w = w.contiguous()
+    d = make_desc(tuple(x.shape), tuple(w.shape), stride, padding, x.dtype)
+    shape = out_shape(tuple(x.shape), tuple(w.shape), stride, padding)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous() \
+            or out.device != x.device:
+        raise ValueError(f"out must be a contiguous {x.dtype} tensor of shape {shape} on {x.device}")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(lib().conv_fwd_path(ctypes.byref(d), PATHS[path], x.data_ptr(), w.data_ptr(),
+                                   out.data_ptr(), stream))
+    return out
+
+
+def from_torch_weight(w_oc_first: torch.Tensor) -> torch.Tensor:
+    """(C_out, C_in, [KD,] KH, KW) PyTorch-style filter -> (C_out, [KD,] KH, KW, C_in)."""
+    perm = (0, *range(2, w_oc_first.dim()), 1)
+    return w_oc_first.permute(perm).contiguous()

@@ -1,0 +1,99 @@
+// conv_device.h -- device helpers shared by the gfx950 convolution kernels:
+// element conversions, output-row decoding, per-dimension tap masks, MFMA
+// wrappers and the XCD-aware tile order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "conv_params.h"
+
+namespace convfwd {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---- element conversions (fp32 accumulation; one RNE rounding on output) ----
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(_Float16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(__bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// v_cvt_f16_f32 rounds to nearest even in the default mode.
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float v) { return (_Float16)v; }
+// gfx950 converts with v_cvt_pk_bf16_f32, round to nearest even.
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return (__bf16)v; }
+
+// ---- output-row decoding ----
+// Output position m = ((n*od + z)*oh + y)*ow + x.  Gives the input origin of
+// its window (the position of tap (0,0,0), possibly in the padding) as an
+// element offset into x, and the per-dimension validity masks: bit t of md is
+// set iff input depth z*sd - pd + t lies inside [0, d), likewise mh and mw.
+struct RowInfo {
+  int base;      // element offset of the window origin (may be negative or past the end)
+  uint32_t md, mh, mw;
+};
+
+// Bits t in [max(0, -i0), min(k, size - i0)) set; k <= 16 (so every shift is < 32).
+__device__ __forceinline__ uint32_t dim_mask(int i0, int k, int size) {
+  const int lo = max(0, -i0);
+  const int hi = min(k, size - i0);
+  if (hi <= lo) return 0u;
+  return ((1u << hi) - 1u) & ~((1u << lo) - 1u);
+}
+
+__device__ __forceinline__ RowInfo decode_row(const ConvParams& p, int m) {
+  RowInfo r;
+  if (m >= p.M) {
+    r.base = 0; r.md = r.mh = r.mw = 0u;
+    return r;
+  }
+  const int xo = m % p.ow;
+  int t = m / p.ow;
+  const int yo = t % p.oh;
+  t /= p.oh;
+  const int zo = t % p.od;
+  const int n = t / p.od;
+  const int z0 = zo * p.sd - p.pd;
+  const int y0 = yo * p.sh - p.ph;
+  const int x0 = xo * p.sw - p.pw;
+  r.base = n * p.xs_n + z0 * p.xs_d + y0 * p.xs_h + x0 * p.xs_w;
+  r.md = dim_mask(z0, p.kd, p.d);
+  r.mh = dim_mask(y0, p.kh, p.h);
+  r.mw = dim_mask(x0, p.kw, p.w);
+  return r;
+}
+
+__device__ __forceinline__ bool tap_valid(const RowInfo& r, int kd, int kh, int kw) {
+  return ((r.md >> kd) & (r.mh >> kh) & (r.mw >> kw) & 1u) != 0u;
+}
+
+// ---- XCD-aware tile order ----
+// Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
+// Give each XCD one contiguous run of tile ids so that the tiles resident on
+// an XCD at the same time are spatial neighbours sharing that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int b, int nblocks) {
+  const int q = nblocks >> 3, rem = nblocks & 7;
+  const int xcd = b & 7, local = b >> 3;
+  return xcd * q + min(xcd, rem) + local;
+}
+
+// ---- MFMA wrappers: D(16x16, fp32) += A(16x32) * B(32x16) ----
+// Lane l supplies row (l % 16) of A and column (l % 16) of B, each as the 8
+// consecutive k in group l / 16; it receives D rows 4*(l/16) .. +3 of column
+// l % 16.
+__device__ __forceinline__ f32x4_t mfma16x16x32(half8_t a, half8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf168_t a, bf168_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T> struct Vec8;
+template <> struct Vec8<_Float16> { typedef half8_t type; };
+template <> struct Vec8<__bf16> { typedef bf168_t type; };
+
+}  // namespace convfwd

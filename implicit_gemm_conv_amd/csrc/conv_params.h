@@ -1,0 +1,44 @@
+// conv_params.h -- problem parameters shared by the host API and the gfx950 kernels.
+//
+// The host derives everything here once per call from the public descriptor
+// (output extents, GEMM sizes, element strides of the channels-last input) and
+// passes the struct to a kernel by value, so kernels read it from the kernel
+// argument segment through scalar loads.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convfwd {
+
+struct ConvParams {
+  int n, d, h, w;          // input extents
+  int cin, cout;           // channels
+  int kd, kh, kw;          // filter extents
+  int sd, sh, sw;          // strides
+  int pd, ph, pw;          // zero padding, both sides
+  int od, oh, ow;          // output extents
+  int M;                   // GEMM rows: n * od * oh * ow
+  int ntaps;               // kd * kh * kw
+  int K;                   // GEMM depth: ntaps * cin (the filter's row length)
+  int xs_w, xs_h, xs_d, xs_n;  // element strides of x along w, h, d, n (xs_w == cin)
+};
+
+enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+// Kernel launchers, one per path.  Each returns hipSuccess or the launch error.
+hipError_t launch_direct(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                         hipStream_t s);
+hipError_t launch_main(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                       hipStream_t s);
+hipError_t launch_flatk(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                        hipStream_t s);
+hipError_t launch_rows(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                       hipStream_t s);
+
+// Whether a path accepts a problem (host-side rules mirrored in convfwd.h).
+bool main_accepts(const ConvParams& p, int dtype);
+bool flatk_accepts(const ConvParams& p, int dtype);
+bool rows_accepts(const ConvParams& p, int dtype);
+
+}  // namespace convfwd

@@ -1,0 +1,177 @@
+// convfwd_api.cpp -- the C ABI declared in include/convfwd.h: descriptor
+// validation, output extents, path selection and the launch on the caller's
+// stream.  No device memory is allocated here and nothing is synchronised.
+#include "../../include/convfwd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "conv_params.h"
+
+using convfwd::ConvParams;
+
+namespace {
+
+// floor((in + 2p - k) / s) + 1, or 0 when the padded input is shorter than the filter.
+int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p) {
+  const int64_t span = in + 2 * p - k;
+  if (span < 0) return 0;
+  return span / s + 1;
+}
+
+int elem_bytes(int dtype) { return dtype == CONVFWD_F32 ? 4 : 2; }
+
+// Validates the descriptor and fills the kernel parameters.  Returns an error
+// code; on success every extent is positive except possibly n (n == 0 is a
+// valid empty problem).
+int make_params(const convfwd_desc* d, ConvParams* p, int64_t* x_bytes, int64_t* w_bytes,
+                int64_t* y_bytes) {
+  if (!d) return CONVFWD_ERR_NULL;
+  if (d->n < 0 || d->d < 1 || d->h < 1 || d->w < 1 || d->c_in < 1 || d->c_out < 1)
+    return CONVFWD_ERR_BAD_DESC;
+  if (d->k_d < 1 || d->k_h < 1 || d->k_w < 1) return CONVFWD_ERR_BAD_DESC;
+  if (d->s_d < 1 || d->s_h < 1 || d->s_w < 1) return CONVFWD_ERR_BAD_DESC;
+  if (d->p_d < 0 || d->p_h < 0 || d->p_w < 0) return CONVFWD_ERR_BAD_DESC;
+  if (d->groups != 1) return CONVFWD_ERR_UNSUPPORTED;
+  if (d->dtype != CONVFWD_F32 && d->dtype != CONVFWD_F16 && d->dtype != CONVFWD_BF16)
+    return CONVFWD_ERR_UNSUPPORTED;
+  const int64_t od = out_extent(d->d, d->k_d, d->s_d, d->p_d);
+  const int64_t oh = out_extent(d->h, d->k_h, d->s_h, d->p_h);
+  const int64_t ow = out_extent(d->w, d->k_w, d->s_w, d->p_w);
+  if (od < 1 || oh < 1 || ow < 1) return CONVFWD_ERR_BAD_DESC;
+
+  const int64_t eb = elem_bytes(d->dtype);
+  const int64_t spatial = (int64_t)d->d * d->h * d->w;
+  const int64_t xe = (int64_t)d->n * spatial * d->c_in;
+  const int64_t ntaps = (int64_t)d->k_d * d->k_h * d->k_w;
+  const int64_t ke = ntaps * d->c_in;
+  const int64_t we = (int64_t)d->c_out * ke;
+  const int64_t M = (int64_t)d->n * od * oh * ow;
+  const int64_t ye = M * d->c_out;
+  const int64_t lim = (int64_t)1 << 31;
+  // 32-bit signed byte offsets inside every tensor; also covers element offsets.
+  if (spatial * d->c_in * eb >= lim || xe * eb >= lim || we * eb >= lim || ye * eb >= lim ||
+      M >= lim || ke >= lim)
+    return CONVFWD_ERR_TOO_LARGE;
+
+  p->n = d->n; p->d = d->d; p->h = d->h; p->w = d->w;
+  p->cin = d->c_in; p->cout = d->c_out;
+  p->kd = d->k_d; p->kh = d->k_h; p->kw = d->k_w;
+  p->sd = d->s_d; p->sh = d->s_h; p->sw = d->s_w;
+  p->pd = d->p_d; p->ph = d->p_h; p->pw = d->p_w;
+  p->od = (int)od; p->oh = (int)oh; p->ow = (int)ow;
+  p->M = (int)M;
+  p->ntaps = (int)ntaps;
+  p->K = (int)ke;
+  p->xs_w = d->c_in;
+  p->xs_h = d->w * d->c_in;
+  p->xs_d = d->h * d->w * d->c_in;
+  p->xs_n = (int)(spatial * d->c_in);
+  *x_bytes = xe * eb;
+  *w_bytes = we * eb;
+  *y_bytes = ye * eb;
+  return CONVFWD_OK;
+}
+
+bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
+}
+
+int auto_path(const ConvParams& p, int dtype) {
+  if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
+  if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;
+  if (convfwd::flatk_accepts(p, dtype)) return CONVFWD_PATH_FLATK;
+  return CONVFWD_PATH_DIRECT;
+}
+
+bool path_accepts(int path, const ConvParams& p, int dtype) {
+  switch (path) {
+    case CONVFWD_PATH_MAIN: return convfwd::main_accepts(p, dtype);
+    case CONVFWD_PATH_FLATK: return convfwd::flatk_accepts(p, dtype);
+    case CONVFWD_PATH_ROWS: return convfwd::rows_accepts(p, dtype);
+    case CONVFWD_PATH_DIRECT: return true;
+    default: return false;
+  }
+}
+
+int run(const convfwd_desc* desc, int path, const void* x, const void* w, void* y, void* stream) {
+  ConvParams p;
+  int64_t xb, wb, yb;
+  const int rc = make_params(desc, &p, &xb, &wb, &yb);
+  if (rc != CONVFWD_OK) return rc;
+  if (path == CONVFWD_PATH_AUTO) path = auto_path(p, desc->dtype);
+  if (!path_accepts(path, p, desc->dtype)) return CONVFWD_ERR_UNSUPPORTED;
+  if (p.n == 0) return CONVFWD_OK;  // empty batch: nothing to read or write
+  if (!x || !w || !y) return CONVFWD_ERR_NULL;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb)) return CONVFWD_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  switch (path) {
+    case CONVFWD_PATH_MAIN: e = convfwd::launch_main(p, desc->dtype, x, w, y, s); break;
+    case CONVFWD_PATH_FLATK: e = convfwd::launch_flatk(p, desc->dtype, x, w, y, s); break;
+    case CONVFWD_PATH_ROWS: e = convfwd::launch_rows(p, desc->dtype, x, w, y, s); break;
+    default: e = convfwd::launch_direct(p, desc->dtype, x, w, y, s); break;
+  }
+  if (e != hipSuccess) return CONVFWD_ERR_LAUNCH;
+  return CONVFWD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int conv_out_shape(const convfwd_desc* desc, int64_t out[5]) {
+  if (!out) return CONVFWD_ERR_NULL;
+  ConvParams p;
+  int64_t xb, wb, yb;
+  const int rc = make_params(desc, &p, &xb, &wb, &yb);
+  if (rc != CONVFWD_OK) return rc;
+  out[0] = p.n; out[1] = p.od; out[2] = p.oh; out[3] = p.ow; out[4] = p.cout;
+  return CONVFWD_OK;
+}
+
+int conv_select_path(const convfwd_desc* desc) {
+  ConvParams p;
+  int64_t xb, wb, yb;
+  const int rc = make_params(desc, &p, &xb, &wb, &yb);
+  if (rc != CONVFWD_OK) return rc;
+  return auto_path(p, desc->dtype);
+}
+
+int conv_fwd(const convfwd_desc* desc, const void* x, const void* w, void* y, void* stream) {
+  return run(desc, CONVFWD_PATH_AUTO, x, w, y, stream);
+}
+
+int conv_fwd_path(const convfwd_desc* desc, int path, const void* x, const void* w, void* y,
+                  void* stream) {
+  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_DIRECT) return CONVFWD_ERR_UNSUPPORTED;
+  return run(desc, path, x, w, y, stream);
+}
+
+const char* conv_strerror(int code) {
+  switch (code) {
+    case CONVFWD_OK: return "success";
+    case CONVFWD_ERR_NULL: return "a required pointer is NULL";
+    case CONVFWD_ERR_BAD_DESC: return "bad descriptor: non-positive extent, stride < 1, pad < 0 or empty output";
+    case CONVFWD_ERR_UNSUPPORTED: return "unsupported: groups != 1, unknown dtype, or the path cannot take this problem";
+    case CONVFWD_ERR_TOO_LARGE: return "too large: a tensor reaches 2^31 bytes or M reaches 2^31";
+    case CONVFWD_ERR_ALIAS: return "the output overlaps an input";
+    case CONVFWD_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+const char* conv_path_name(int path) {
+  switch (path) {
+    case CONVFWD_PATH_AUTO: return "auto";
+    case CONVFWD_PATH_MAIN: return "main";
+    case CONVFWD_PATH_FLATK: return "flatk";
+    case CONVFWD_PATH_ROWS: return "rows";
+    case CONVFWD_PATH_DIRECT: return "direct";
+    default: return "unknown";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+/*
+ * convfwd.h -- C ABI of the channels-last implicit-GEMM convolution forward
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (the "Convolutions" tutorial page, sections 1 and 4, and the
+ * MLX pull request "Add implicit matmul pathway for mx.conv3d", benchmark
+ * table header for the layouts): for every output position and output
+ * channel,
+ *
+ *   y[n,od,oh,ow,co] = sum_{kd,kh,kw,c} X(n, od*s_d - p_d + kd,
+ *                                          oh*s_h - p_h + kh,
+ *                                          ow*s_w - p_w + kw, c) * w[co,kd,kh,kw,c]
+ *
+ * with X the input extended by zeros outside its extent.  The filter is not
+ * flipped (the tutorial's worked example fixes the orientation).  Output
+ * extents are floor((in + 2p - k)/s) + 1.  The result is computed as an
+ * implicit GEMM (tutorial section 5, "Alternatives"): M = N*D_out*H_out*W_out
+ * rows, N_gemm = C_out columns, K = C_in*K_d*K_h*K_w, with the im2col operand
+ * addressed on the fly inside the kernel and never stored.
+ *
+ * Layouts (all dense, innermost dimension last, no padding between rows):
+ *   x  (N, D, H, W, C_in)                   channels-last input
+ *   w  (C_out, K_d, K_h, K_w, C_in)         filter, C_in fastest
+ *   y  (N, D_out, H_out, W_out, C_out)      channels-last output, same dtype as x
+ * A 2D problem is the 3D one with d = k_d = s_d = 1 and p_d = 0.
+ *
+ * Arithmetic: fp16 and bf16 inputs are multiplied exactly and accumulated in
+ * fp32; the result is rounded once to the output dtype, round-to-nearest-even.
+ * fp32 inputs are accumulated in fp32.  The summation order is unspecified.
+ *
+ * Ownership: the caller owns x, w, y and the stream.  The library allocates
+ * no device memory (no workspace, no im2col buffer), never frees, never
+ * synchronises and keeps no mutable state, so calls are reentrant and may be
+ * made from several host threads.
+ *
+ * Errors: every entry point validates its arguments before touching the GPU
+ * and returns 0 or one of the negative codes below.  Faults inside a kernel
+ * are asynchronous: they surface at the caller's next synchronisation on the
+ * stream, not in a return code.
+ */
+#ifndef CONVFWD_H
+#define CONVFWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CONVFWD_F32 = 0,
+  CONVFWD_F16 = 1,
+  CONVFWD_BF16 = 2
+} convfwd_dtype;
+
+/* Return codes. */
+enum {
+  CONVFWD_OK = 0,
+  CONVFWD_ERR_NULL = -1,        /* a required pointer is NULL */
+  CONVFWD_ERR_BAD_DESC = -2,    /* a non-positive extent, stride < 1, pad < 0, or an empty output */
+  CONVFWD_ERR_UNSUPPORTED = -3, /* groups != 1, unknown dtype, or a path that cannot take this problem */
+  CONVFWD_ERR_TOO_LARGE = -4,   /* a tensor of 2^31 bytes or more, or M >= 2^31 */
+  CONVFWD_ERR_ALIAS = -5,       /* y's byte range overlaps x or w */
+  CONVFWD_ERR_LAUNCH = -6       /* the HIP runtime refused the launch */
+};
+
+/* Kernel paths.  AUTO lets the library choose; the others force one (for
+ * testing every path on every shape it accepts). */
+typedef enum {
+  CONVFWD_PATH_AUTO = 0,
+  CONVFWD_PATH_MAIN = 1,   /* fp16/bf16, C_in % 64 == 0, C_out % 4 == 0, filter <= 16 per dim:
+                              16-byte channels-last loads straight into LDS, MFMA */
+  CONVFWD_PATH_FLATK = 2,  /* any C_in (the unaligned-channel tail path), filter <= 16 per dim:
+                              element-granular gathers over the flattened (tap, channel) axis, MFMA */
+  CONVFWD_PATH_ROWS = 3,   /* fp16/bf16 tiny C_in (C_in * K_w <= 64, 2D or 3D): whole input rows
+                              staged in LDS, MFMA */
+  CONVFWD_PATH_DIRECT = 4  /* any problem: one thread per output, fp32 FMA (slow, simple) */
+} convfwd_path;
+
+/* Problem descriptor.  All extents in elements. */
+typedef struct {
+  int32_t n, d, h, w;        /* input batch and spatial extents (d = 1 for 2D) */
+  int32_t c_in, c_out;       /* channels */
+  int32_t k_d, k_h, k_w;     /* filter extents (k_d = 1 for 2D) */
+  int32_t s_d, s_h, s_w;     /* strides, >= 1 */
+  int32_t p_d, p_h, p_w;     /* zero padding added on both sides, >= 0 */
+  int32_t groups;            /* must be 1 */
+  int32_t dtype;             /* convfwd_dtype; x, w and y share it */
+} convfwd_desc;
+
+/* Output shape (N, D_out, H_out, W_out, C_out) into out[5].  Host only; never
+ * touches the GPU.  Returns CONVFWD_OK or a validation error. */
+int conv_out_shape(const convfwd_desc* desc, int64_t out[5]);
+
+/* The path CONVFWD_PATH_AUTO would take for this descriptor (a positive
+ * convfwd_path), or a negative validation error.  Host only. */
+int conv_select_path(const convfwd_desc* desc);
+
+/* y = conv(x, w) on `stream` (a hipStream_t; NULL means the null stream of the
+ * current device).  x, w, y are device pointers on the current device, laid
+ * out as above, with at least 2-byte (fp16/bf16) or 4-byte (fp32) alignment.
+ * Asynchronous: returns after the launch.  With N = 0 it launches nothing and
+ * returns CONVFWD_OK without reading the pointers. */
+int conv_fwd(const convfwd_desc* desc, const void* x, const void* w, void* y, void* stream);
+
+/* As conv_fwd, but on the given path; CONVFWD_ERR_UNSUPPORTED if that path
+ * cannot take the problem. */
+int conv_fwd_path(const convfwd_desc* desc, int path, const void* x, const void* w, void* y,
+                  void* stream);
+
+/* Static message for a return code; never NULL. */
+const char* conv_strerror(int code);
+
+/* Static name of a path ("main", "flatk", "rows", "direct", "auto"); never NULL. */
+const char* conv_path_name(int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVFWD_H */

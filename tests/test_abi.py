@@ -1,0 +1,163 @@
+"""Host-side tests of the C ABI (no GPU needed): symbols, shapes, validation, path choice.
+
+Every call made here returns before the library touches the GPU: descriptor
+validation, output extents, path selection, the empty-batch no-op and the
+pointer checks all run on the host first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import implicit_gemm_conv_amd as igc
+import oracle
+from conv_workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convfwd.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(conv_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert names == sorted(n for n, _, _ in igc.EXPORTS)
+    lib = igc.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _desc(**kw):
+    base = dict(n=2, d=4, h=5, w=6, c_in=8, c_out=4, k_d=3, k_h=3, k_w=3, s_d=1, s_h=1, s_w=1,
+                p_d=1, p_h=1, p_w=1, groups=1, dtype=1)
+    base.update(kw)
+    return igc.Desc(**base)
+
+
+def _out_shape(d):
+    out = (ctypes.c_int64 * 5)()
+    rc = igc.lib().conv_out_shape(ctypes.byref(d), out)
+    return rc, tuple(out)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_out_shape_matches_oracle_extents(name):
+    wl = WORKLOADS[name]
+    got = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding)
+    sp = wl.x_shape[1:-1]
+    ks = wl.w_shape[1:-1]
+    expect = (wl.x_shape[0], *[oracle.out_extent(sp[i], ks[i], wl.stride[i], wl.padding[i])
+                               for i in range(wl.dims)], wl.w_shape[0])
+    assert got == expect
+
+
+def test_out_shape_table_from_pages():
+    assert igc.out_shape((64, 224, 224, 3), (64, 7, 7, 3), 2, 3) == (64, 112, 112, 64)
+    assert igc.out_shape((4, 32, 32, 32, 64), (128, 3, 3, 3, 64), 2, 1) == (4, 16, 16, 16, 128)
+    assert igc.out_shape((1, 3, 3, 1), (1, 2, 2, 1), 1, 0) == (1, 2, 2, 1)
+    assert igc.out_shape((1, 5, 5, 1), (1, 3, 3, 1), 1, 0) == (1, 3, 3, 1)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d", 0, -2), ("h", -1, -2), ("c_in", 0, -2), ("c_out", 0, -2), ("k_w", 0, -2),
+    ("s_h", 0, -2), ("p_d", -1, -2), ("n", -1, -2),
+    ("k_h", 12, -2),            # 5 + 2 < 12: empty output
+    ("groups", 2, -3), ("dtype", 7, -3),
+])
+def test_validation_codes(field, value, code):
+    rc, _ = _out_shape(_desc(**{field: value}))
+    assert rc == code
+    assert igc.lib().conv_fwd(ctypes.byref(_desc(**{field: value})), 16, 4096, 1 << 20, None) == code
+
+
+def test_null_arguments():
+    lib = igc.lib()
+    assert lib.conv_out_shape(None, (ctypes.c_int64 * 5)()) == -1
+    assert lib.conv_out_shape(ctypes.byref(_desc()), None) == -1
+    assert lib.conv_fwd(None, 16, 16, 16, None) == -1
+    assert lib.conv_fwd(ctypes.byref(_desc()), None, 4096, 1 << 20, None) == -1
+    assert lib.conv_fwd(ctypes.byref(_desc()), 16, 4096, None, None) == -1
+
+
+def test_too_large():
+    # 2^31 bytes of fp16 input
+    d = _desc(n=1, d=1, h=1 << 15, w=1 << 15, c_in=1, c_out=1, k_d=1, k_h=1, k_w=1, p_d=0, p_h=0, p_w=0)
+    assert _out_shape(d)[0] == -4
+    d = _desc(n=1, d=1, h=1 << 14, w=1 << 15, c_in=1, c_out=1, k_d=1, k_h=1, k_w=1, p_d=0, p_h=0, p_w=0)
+    assert _out_shape(d)[0] == 0
+
+
+def test_alias_rejected_before_launch():
+    lib = igc.lib()
+    d = _desc()
+    xb = 2 * 4 * 5 * 6 * 8 * 2
+    base = 1 << 24
+    # y starting inside x
+    assert lib.conv_fwd(ctypes.byref(d), base, base + (1 << 20), base + xb - 2, None) == -5
+    # y covering w
+    assert lib.conv_fwd(ctypes.byref(d), base, base + (1 << 20), base + (1 << 20) - 64, None) == -5
+
+
+def test_empty_batch_is_a_no_op():
+    lib = igc.lib()
+    d = _desc(n=0)
+    rc, shape = _out_shape(d)
+    assert rc == 0 and shape[0] == 0
+    assert lib.conv_fwd(ctypes.byref(d), None, None, None, None) == 0
+
+
+def test_forced_path_rules():
+    lib = igc.lib()
+    # main path needs C_in % 64 == 0 and fp16/bf16
+    d = _desc(c_in=65, n=0)
+    assert lib.conv_fwd_path(ctypes.byref(d), 1, None, None, None, None) == -3
+    d = _desc(c_in=64, dtype=0, n=0)
+    assert lib.conv_fwd_path(ctypes.byref(d), 1, None, None, None, None) == -3
+    d = _desc(c_in=64, n=0)
+    assert lib.conv_fwd_path(ctypes.byref(d), 1, None, None, None, None) == 0
+    assert lib.conv_fwd_path(ctypes.byref(d), 99, None, None, None, None) == -3
+    # filters wider than 16 only on the direct path
+    d = _desc(n=0, w=40, k_w=17)
+    assert lib.conv_fwd_path(ctypes.byref(d), 2, None, None, None, None) == -3
+    assert lib.conv_fwd_path(ctypes.byref(d), 4, None, None, None, None) == 0
+
+
+def test_strerror_and_path_names():
+    lib = igc.lib()
+    for code in range(-7, 1):
+        assert lib.conv_strerror(code)
+    assert [lib.conv_path_name(i).decode() for i in range(5)] == ["auto", "main", "flatk", "rows",
+                                                                  "direct"]
+
+
+EXPECTED_PATHS = {
+    "c1_conv3d_fp32_n1_8c16_o32": "flatk",
+    "c2_conv2d_fp16_n32_56c256_o256": "main",
+    "c4a_conv3d_fp16_n4_32c128_o128": "main",
+    "c4b_conv3d_fp16_n1_64c64_o128": "main",
+    "c4c_conv3d_fp16_n4_32c64_o128_s2": "main",
+    "c5a_conv3d_bf16_n4_32c65_o65": "flatk",
+    "c5b_conv3d_bf16_n4_16c21_o21": "flatk",
+    "c5c_conv3d_bf16_n4_32c64_o128_k311": "main",
+    "c5d_conv3d_bf16_n4_32c64_o128_k133": "main",
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXPECTED_PATHS))
+def test_auto_path_choice(name):
+    wl = WORKLOADS[name]
+    assert igc.select_path(wl.x_shape, wl.w_shape, wl.stride, wl.padding,
+                           wl.torch_dtype) == EXPECTED_PATHS[name]
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(1, 4, 4, 4, dtype=torch.float16)
+    w = torch.zeros(4, 3, 3, 4, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        igc.conv_fwd(x, w, 1, 1)

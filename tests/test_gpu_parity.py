@@ -1,0 +1,206 @@
+"""GPU parity: the HIP library against the float64 oracle, element by element.
+
+Every case draws seeded inputs from conv_workloads, runs the library through
+the C ABI (via the thin Python binding) on one forced path or on the path the
+library picks, and compares with the oracle under the tolerances in
+tests/parity.py.  Integer-valued cases (tap counts, one-hot gathers) are
+compared bit for bit.  Full-size workloads run in the launch configuration the
+bench times and are checked on sampled output rows the oracle computes one by
+one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import implicit_gemm_conv_amd as igc
+import oracle
+from conv_workloads import WORKLOADS, Workload, make_inputs
+from tests.parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _case(name, dtype, xs, ws, st, pd, x_dist="uniform", seed=7):
+    return Workload(name, dtype, tuple(xs), tuple(ws), tuple(st), tuple(pd), x_dist,
+                    seed * 10 + 1, seed * 10 + 2)
+
+
+# Reduced shapes: several tiles plus ragged M (and N) tails, same channel and
+# filter structure as the full workloads, plus the degenerate cases.
+CASES = [
+    _case("c4_like_fp16_c64", "fp16", (2, 9, 10, 11, 64), (128, 3, 3, 3, 64), (1, 1, 1), (1, 1, 1), seed=1),
+    _case("c4a_like_fp16_c128", "fp16", (1, 6, 7, 9, 128), (128, 3, 3, 3, 128), (1, 1, 1), (1, 1, 1), seed=2),
+    _case("c4c_like_fp16_s2", "fp16", (2, 11, 12, 13, 64), (128, 3, 3, 3, 64), (2, 2, 2), (1, 1, 1), seed=3),
+    _case("c5c_like_bf16_k311", "bf16", (2, 8, 9, 10, 64), (128, 3, 1, 1, 64), (1, 1, 1), (1, 0, 0), seed=4),
+    _case("c5d_like_bf16_k133", "bf16", (2, 8, 9, 10, 64), (128, 1, 3, 3, 64), (1, 1, 1), (0, 1, 1), seed=5),
+    _case("c2_like_fp16_2d_c256_o96", "fp16", (3, 13, 14, 256), (96, 3, 3, 256), (1, 1), (1, 1), seed=6),
+    _case("fp16_2d_o4", "fp16", (2, 9, 9, 64), (4, 3, 3, 64), (1, 1), (1, 1), seed=7),
+    _case("fp16_2d_o260", "fp16", (1, 7, 9, 128), (260, 3, 3, 128), (1, 1), (1, 1), seed=8),
+    _case("fp16_s3_pad3", "fp16", (1, 7, 8, 9, 64), (64, 3, 3, 3, 64), (3, 3, 3), (3, 3, 3), seed=9),
+    _case("bf16_2d_k5", "bf16", (2, 12, 13, 64), (32, 5, 5, 64), (1, 1), (2, 2), seed=10),
+    _case("c5a_like_bf16_c65", "bf16", (2, 7, 8, 9, 65), (65, 3, 3, 3, 65), (1, 1, 1), (1, 1, 1), seed=11),
+    _case("c5b_like_bf16_c21", "bf16", (3, 6, 7, 8, 21), (21, 3, 3, 3, 21), (1, 1, 1), (1, 1, 1), seed=12),
+    _case("c3_like_fp16_stem", "fp16", (2, 30, 31, 3), (64, 7, 7, 3), (2, 2), (3, 3), "normal", seed=13),
+    _case("c1_fp32", "fp32", (1, 8, 8, 8, 16), (32, 3, 3, 3, 16), (1, 1, 1), (1, 1, 1), seed=14),
+    _case("fp32_odd", "fp32", (2, 5, 6, 7, 5), (7, 3, 2, 3, 5), (1, 2, 1), (1, 0, 2), seed=15),
+    _case("fp16_c16", "fp16", (2, 6, 6, 6, 16), (32, 3, 3, 3, 16), (1, 1, 1), (1, 1, 1), seed=16),
+    _case("bf16_c1_single_output", "bf16", (1, 3, 3, 1), (1, 3, 3, 1), (1, 1), (0, 0), seed=17),
+    _case("fp16_1x1_pointwise", "fp16", (2, 5, 7, 64), (64, 1, 1, 64), (1, 1), (0, 0), seed=18),
+]
+PATHS = ["main", "flatk", "direct"]
+
+
+def _accepts(wl, path):
+    if path == "main":
+        return wl.dtype in ("fp16", "bf16") and wl.x_shape[-1] % 64 == 0 and wl.w_shape[0] % 4 == 0
+    return True
+
+
+def _run(wl, path="auto", x=None, w=None):
+    if x is None:
+        x, w = make_inputs(wl, DEV)
+    y = igc.conv_fwd(x, w, wl.stride, wl.padding, path=path)
+    torch.cuda.synchronize()
+    return x, w, y
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("wl", CASES, ids=[c.name for c in CASES])
+def test_parity_reduced(wl, path):
+    if not _accepts(wl, path):
+        pytest.skip(f"{path} does not take {wl.name}")
+    print(f"[parity] {wl.name} path={path}", flush=True)
+    x, w, y = _run(wl, path)
+    ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), wl.stride, wl.padding)
+    assert_parity(oracle.to_float64(y), ref, wl.dtype, f"{wl.name}/{path}")
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[c.name for c in CASES])
+def test_auto_path_is_deterministic(wl):
+    x, w, y1 = _run(wl)
+    _, _, y2 = _run(wl, x=x, w=w)
+    assert torch.equal(y1.view(torch.uint8) if y1.dtype != torch.float32 else y1.view(torch.int32),
+                       y2.view(torch.uint8) if y2.dtype != torch.float32 else y2.view(torch.int32))
+
+
+def _sample_rows(m_total, count, seed):
+    rng = np.random.default_rng(seed)
+    edge = np.concatenate([np.arange(min(64, m_total)), np.arange(max(0, m_total - 64), m_total)])
+    rand = rng.integers(0, m_total, size=count)
+    return np.unique(np.concatenate([edge, rand]))
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_parity_full_size_sampled(name):
+    """Full-size workloads on the auto path (the launch the bench times), checked on
+    sampled output rows: the first and last 64 plus 2048 random ones."""
+    wl = WORKLOADS[name]
+    print(f"[full] {name} path={igc.select_path(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.torch_dtype)}",
+          flush=True)
+    x, w, y = _run(wl)
+    yf = y.reshape(-1, y.shape[-1])
+    rows = _sample_rows(yf.shape[0], 2048, seed=wl.seed_x)
+    ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), wl.stride, wl.padding, rows=rows)
+    got = oracle.to_float64(yf[torch.from_numpy(rows).to(DEV)])
+    assert_parity(got, ref, wl.dtype, name)
+    # every output is finite
+    assert torch.isfinite(y.float()).all()
+
+
+# ---- bit-exact index and boundary handling ----------------------------------------
+
+EXACT = [
+    ("main", "fp16", (2, 5, 6, 7, 64), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
+    ("main", "bf16", (1, 6, 7, 9, 64), (3, 3, 3), (2, 2, 2), (2, 1, 3)),
+    ("flatk", "bf16", (2, 5, 6, 7, 5), (3, 3, 3), (1, 2, 1), (1, 1, 2)),
+    ("flatk", "fp32", (1, 4, 9, 8, 3), (1, 7, 7), (1, 2, 2), (0, 3, 3)),
+    ("flatk", "fp16", (2, 5, 6, 7, 65), (3, 3, 3), (3, 1, 2), (3, 1, 0)),
+    ("direct", "fp16", (1, 5, 6, 7, 3), (3, 3, 3), (2, 2, 2), (1, 1, 1)),
+]
+
+
+def _dt(name):
+    return {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}[name]
+
+
+@pytest.mark.parametrize("path,dtype,xs,ks,st,pd", EXACT)
+def test_tap_count_bit_exact(path, dtype, xs, ks, st, pd):
+    """x = 1, w = 1 on input channel 0 only: every output is its number of in-bounds taps."""
+    cin = xs[-1]
+    cout = 8
+    x = torch.ones(xs, dtype=_dt(dtype), device=DEV)
+    w = torch.zeros((cout, *ks, cin), dtype=_dt(dtype), device=DEV)
+    w[..., 0] = 1
+    y = igc.conv_fwd(x, w, st, pd, path=path)
+    torch.cuda.synchronize()
+    ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), st, pd)
+    np.testing.assert_array_equal(oracle.to_float64(y), ref)
+
+
+@pytest.mark.parametrize("path,dtype,xs,ks,st,pd", EXACT)
+def test_one_hot_gather_bit_exact(path, dtype, xs, ks, st, pd):
+    """w = identity on channels at one tap: y is a shifted, strided copy of x (0 in the padding)."""
+    c = xs[-1]
+    g = torch.Generator("cpu").manual_seed(99)
+    x = (torch.rand(xs, generator=g) * 2 - 1).to(_dt(dtype)).to(DEV)
+    taps = [(0, 0, 0), tuple(k - 1 for k in ks), tuple(k // 2 for k in ks)]
+    for tap in taps:
+        w = torch.zeros((c, *ks, c), dtype=_dt(dtype))
+        w[(torch.arange(c), *[torch.full((c,), t) for t in tap], torch.arange(c))] = 1
+        w = w.to(DEV)
+        y = igc.conv_fwd(x, w, st, pd, path=path)
+        torch.cuda.synchronize()
+        ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), st, pd)
+        np.testing.assert_array_equal(oracle.to_float64(y), ref, err_msg=f"tap {tap}")
+
+
+# ---- boundary behaviour -------------------------------------------------------------
+
+def test_empty_batch_launches_nothing():
+    x = torch.empty((0, 4, 4, 4, 64), dtype=torch.float16, device=DEV)
+    w = torch.randn((64, 3, 3, 3, 64), device=DEV).half()
+    y = igc.conv_fwd(x, w, 1, 1)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 4, 4, 4, 64)
+
+
+def test_non_contiguous_inputs_are_made_contiguous():
+    wl = CASES[0]
+    x, w = make_inputs(wl, DEV)
+    xt = x.permute(0, 2, 1, 3, 4).contiguous().permute(0, 2, 1, 3, 4)   # same values, strided
+    assert not xt.is_contiguous()
+    y = igc.conv_fwd(xt, w, wl.stride, wl.padding)
+    y0 = igc.conv_fwd(x, w, wl.stride, wl.padding)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+
+
+def test_no_workspace_and_no_out_of_bounds_writes():
+    """The call allocates nothing and writes only inside y (canaries around it stay intact)."""
+    wl = CASES[2]
+    x, w = make_inputs(wl, DEV)
+    shape = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding)
+    n = int(np.prod(shape))
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), 12345.0, dtype=torch.float16, device=DEV)
+    y = buf[guard:guard + n].view(shape)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    igc.conv_fwd(x, w, wl.stride, wl.padding, out=y)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    assert torch.all(buf[:guard] == 12345.0) and torch.all(buf[guard + n:] == 12345.0)
+    ref = igc.conv_fwd(x, w, wl.stride, wl.padding)
+    torch.cuda.synchronize()
+    assert torch.equal(y, ref)
+
+
+def test_wrong_out_rejected():
+    x = torch.zeros((1, 4, 4, 4, 64), dtype=torch.float16, device=DEV)
+    w = torch.zeros((64, 3, 3, 3, 64), dtype=torch.float16, device=DEV)
+    with pytest.raises(ValueError):
+        igc.conv_fwd(x, w, 1, 1, out=torch.empty((1, 4, 4, 4, 63), dtype=torch.float16, device=DEV))
+    with pytest.raises(igc.ConvError):
+        igc.conv_fwd(x, w, 1, 1, path="rows")
