@@ -49,20 +49,28 @@ def kernel_key(wl):
     return igc.select_path(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.torch_dtype)
 
 
-def cpu_baseline(wl, x, w, rows_count=4096):
+def cpu_baseline(wls, inputs, fraction):
+    """The oracle on `fraction` of the output rows of every convolution of one step
+    (evenly spaced rows, all channels); 1.0 is one whole step."""
     import oracle
-    xf = oracle.to_float64(x)
-    wf = oracle.to_float64(w)
-    m, n, k = gemm_dims(wl)
-    rows = np.linspace(0, m - 1, rows_count).astype(np.int64)
     threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    t0 = time.perf_counter()
-    oracle.conv_fwd(xf, wf, wl.stride, wl.padding, rows=rows)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows_count * n * k
+    flops, dt, rows_done, rows_all = 0.0, 0.0, 0, 0
+    for wl, (x, w) in zip(wls, inputs):
+        xf = oracle.to_float64(x)
+        wf = oracle.to_float64(w)
+        m, n, k = gemm_dims(wl)
+        count = max(1, int(round(m * fraction)))
+        rows = np.linspace(0, m - 1, count).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.conv_fwd(xf, wf, wl.stride, wl.padding, rows=rows)
+        dt += time.perf_counter() - t0
+        flops += 2.0 * count * n * k
+        rows_done += count
+        rows_all += m
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{wl.name}: {rows_count} of {m} output rows (evenly spaced), all {n} "
-                      f"channels, float64 direct loop; {dt:.2f} s"}
+            "sample": f"{rows_done} of the {rows_all} output rows of one step (the three "
+                      f"convolutions, evenly spaced rows, all channels), float64 direct loop, "
+                      f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
 
 
 def main():
@@ -71,7 +79,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=65536)
+    ap.add_argument("--cpu-fraction", type=float, default=1.0,
+                    help="share of one step's output rows the CPU oracle computes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -152,8 +161,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        x0, w0 = inputs[0]
-        rec["cpu_baseline"] = cpu_baseline(wls[0], x0, w0, args.cpu_rows)
+        rec["cpu_baseline"] = cpu_baseline(wls, inputs, args.cpu_fraction)
     print(json.dumps(rec), flush=True)
 
 
