@@ -13,6 +13,7 @@ namespace convfwd {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf168_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---- element conversions (fp32 accumulation; one RNE rounding on output) ----
@@ -90,6 +91,16 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(half8_t a, half8_t b, f32x4_t c)
 }
 __device__ __forceinline__ f32x4_t mfma16x16x32(bf168_t a, bf168_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32, fp32) += A(32x16) * B(16x32).  Lane l supplies row (l % 32) of A
+// and column (l % 32) of B, each as the 8 consecutive k of group l / 32; it
+// receives column l % 32 of D, rows 8q + 4*(l/32) + i in element 4q + i.
+__device__ __forceinline__ f32x16_t mfma32x32x16(half8_t a, half8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf168_t a, bf168_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 template <typename T> struct Vec8;

@@ -80,6 +80,8 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
 }
 
 int auto_path(const ConvParams& p, int dtype) {
+  const bool unit_stride = p.sd == 1 && p.sh == 1 && p.sw == 1;
+  if (unit_stride && convfwd::brick_accepts(p, dtype)) return CONVFWD_PATH_BRICK;
   if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;
   if (convfwd::flatk_accepts(p, dtype)) return CONVFWD_PATH_FLATK;
@@ -92,6 +94,7 @@ bool path_accepts(int path, const ConvParams& p, int dtype) {
     case CONVFWD_PATH_FLATK: return convfwd::flatk_accepts(p, dtype);
     case CONVFWD_PATH_ROWS: return convfwd::rows_accepts(p, dtype);
     case CONVFWD_PATH_DIRECT: return true;
+    case CONVFWD_PATH_BRICK: return convfwd::brick_accepts(p, dtype);
     default: return false;
   }
 }
@@ -112,6 +115,7 @@ int run(const convfwd_desc* desc, int path, const void* x, const void* w, void* 
     case CONVFWD_PATH_MAIN: e = convfwd::launch_main(p, desc->dtype, x, w, y, s); break;
     case CONVFWD_PATH_FLATK: e = convfwd::launch_flatk(p, desc->dtype, x, w, y, s); break;
     case CONVFWD_PATH_ROWS: e = convfwd::launch_rows(p, desc->dtype, x, w, y, s); break;
+    case CONVFWD_PATH_BRICK: e = convfwd::launch_brick(p, desc->dtype, x, w, y, s); break;
     default: e = convfwd::launch_direct(p, desc->dtype, x, w, y, s); break;
   }
   if (e != hipSuccess) return CONVFWD_ERR_LAUNCH;
@@ -146,7 +150,7 @@ int conv_fwd(const convfwd_desc* desc, const void* x, const void* w, void* y, vo
 
 int conv_fwd_path(const convfwd_desc* desc, int path, const void* x, const void* w, void* y,
                   void* stream) {
-  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_DIRECT) return CONVFWD_ERR_UNSUPPORTED;
+  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_BRICK) return CONVFWD_ERR_UNSUPPORTED;
   return run(desc, path, x, w, y, stream);
 }
 
@@ -170,6 +174,7 @@ const char* conv_path_name(int path) {
     case CONVFWD_PATH_FLATK: return "flatk";
     case CONVFWD_PATH_ROWS: return "rows";
     case CONVFWD_PATH_DIRECT: return "direct";
+    case CONVFWD_PATH_BRICK: return "brick";
     default: return "unknown";
   }
 }

@@ -1,27 +1,32 @@
-// k_main.hip -- the main implicit-GEMM path for fp16/bf16 with C_in % 64 == 0.
+// k_main.hip -- the main implicit-GEMM path for fp16/bf16 with C_in % BK == 0.
 //
 // GEMM view ("Convolutions" tutorial, section 5, implicit GEMM): row m of the
 // virtual im2col matrix is output position m, column k = (tap, c).  A K step
-// covers 64 channels of one tap, so every A row segment is 128 contiguous
-// bytes of the channels-last input and every B row segment 128 contiguous
-// bytes of the filter.
+// covers BK (32 or 64) channels of one tap, so every A row segment is BK*2
+// contiguous bytes of the channels-last input and every B row segment BK*2
+// contiguous bytes of the filter.
 //
 // Per workgroup (256 threads = 4 waves of 64):
 //  * tile BM x BN of the output; tile ids follow the XCD-aware order;
 //  * once per tile, each loader thread decodes its output rows into a window
 //    origin plus three per-dimension validity masks (the precomputed pad and
 //    stride masks); per K step a row's tap is valid iff one bit of each mask
-//    is set, else the lane reads a 16-byte zero block instead of the input;
-//  * operands move global -> LDS with 16-byte direct-to-LDS loads
-//    (global_load_lds_dwordx4), STAGES buffers deep, so the loads of the next
-//    steps are in flight while the current one is multiplied;
-//  * LDS rows hold 64 channels (8 chunks of 16 B) with the chunk index XORed
-//    by (row & 7), so the 16-byte fragment reads of 8 consecutive rows hit
-//    distinct banks;
-//  * each wave multiplies a (BM/WM) x (BN/WN) sub-tile with
-//    v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulators.  The filter fragment
-//    is the MFMA's first operand, so a lane ends up holding 4 consecutive
-//    output channels of one output row and stores them as one 8-byte write.
+//    is set;
+//  * operands move global -> LDS with 16-byte buffer loads that write LDS
+//    directly (buffer_load_dwordx4 ... lds), STAGES buffers deep, so the
+//    loads of the next steps are in flight while the current one is
+//    multiplied.  A lane whose tap falls in the padding gets an offset past
+//    the end of the buffer, and the hardware's range check returns zeros;
+//  * LDS rows hold BK channels in 16-byte chunks whose index is XORed with a
+//    function of the row, so the 16-byte fragment reads of 8 consecutive rows
+//    cover all banks;
+//  * each wave multiplies a (BM/WM) x (BN/WN) sub-tile in MF x MF blocks,
+//    v_mfma_f32_32x32x16 (MF = 32) or v_mfma_f32_16x16x32 (MF = 16), fp32
+//    accumulators.  On gfx950 one wave can keep the matrix unit busy with
+//    independent 32x32x16 MFMAs, while 16x16x32 needs two waves per SIMD.
+//    The filter fragment is the MFMA's first operand, so a lane ends up
+//    holding runs of 4 consecutive output channels of one output row and
+//    stores each run as one 8-byte write.
 // The K loop runs channel chunks in the outer position and taps in the inner
 // one, so consecutive steps re-read input rows shifted by one tap, which the
 // caches still hold.
@@ -31,9 +36,12 @@ namespace convfwd {
 
 namespace {
 
-__device__ __attribute__((aligned(64))) uint32_t g_zero_block[16];  // 64 zero bytes
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Offset that fails the buffer range check (every tensor is < 2^31 bytes).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+// Buffer resource word 3 for raw (untyped, unswizzled) buffers on gfx9 parts.
+constexpr int kRawBufferFlags = 0x00020000;
 
 // Waits until at most N of this thread's vector-memory operations are
 // outstanding, then joins the workgroup barrier.  One asm block (with a
@@ -45,21 +53,53 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int STAGES>
-__global__ __launch_bounds__(256) void conv_main_kernel(ConvParams p, const T* __restrict__ x,
-                                                        const T* __restrict__ w,
-                                                        T* __restrict__ y, int tiles_n) {
+// Physical 16-byte chunk of logical chunk `lc` in LDS row `r` for rows of
+// CPR chunks: 8 consecutive rows reading the same logical chunk must land
+// on 8 different 16-byte bank groups of a 128-byte bank line.
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int lc) {
+  if constexpr (CPR == 8) return lc ^ (r & 7);
+  else return lc ^ ((r >> 1) & 3);   // two 64-byte rows share a bank line
+}
+
+template <int MF> struct Acc;
+template <> struct Acc<16> { typedef f32x4_t type; };
+template <> struct Acc<32> { typedef f32x16_t type; };
+
+template <typename V8, typename A>
+__device__ __forceinline__ A mfma_block(V8 a, V8 b, A c) {
+  if constexpr (sizeof(A) == 16) return mfma16x16x32(a, b, c);
+  else return mfma32x32x16(a, b, c);
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int MF>
+__global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const T* __restrict__ x,
+                                                             const T* __restrict__ w,
+                                                             T* __restrict__ y, int tiles_n,
+                                                             uint32_t x_bytes, uint32_t w_bytes) {
+  // The body uses buffer-resource builtins that exist only for the GPU; the
+  // host pass needs nothing but the kernel's signature to emit its launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
   typedef typename Vec8<T>::type V8;
-  constexpr int BK = 64;                // channels per K step
+  typedef typename Acc<MF>::type AccT;
   constexpr int ROWB = BK * 2;          // LDS bytes per tile row
-  constexpr int A_LOADS = BM / 32;      // 16-byte loads per thread per step
-  constexpr int B_LOADS = BN / 32;
+  constexpr int CPR = BK / 8;           // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;         // rows one wave instruction fills
+  constexpr int RPR = 4 * RPI;          // rows the workgroup fills per load round
+  constexpr int A_LOADS = BM / RPR;     // 16-byte loads per thread per step
+  constexpr int B_LOADS = BN / RPR;
   constexpr int NL = A_LOADS + B_LOADS;
   constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int FM = TM / MF, FN = TN / MF;
+  constexpr int KSUB = MF == 32 ? 16 : 32;   // k per MFMA
+  constexpr int LG = 64 / MF;                 // lane groups along k (2 or 4)
+  constexpr int NQ = MF == 32 ? 4 : 1;        // runs of 4 channels per lane per block
+  constexpr int NACC = MF == 32 ? 16 : 4;
   constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(BM % RPR == 0 && BN % RPR == 0, "loader rounds");
   static_assert(WM * WN == 4, "4 waves");
-  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
+  static_assert(TM % MF == 0 && TN % MF == 0, "wave tile");
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   static_assert(NL * (STAGES - 2) < 64, "vmcnt");
 
@@ -72,22 +112,30 @@ __global__ __launch_bounds__(256) void conv_main_kernel(ConvParams p, const T* _
   const int m0 = (tile / tiles_n) * BM;
   const int n0 = (tile % tiles_n) * BN;
 
-  // Loader geometry: a wave's load instruction fills 8 consecutive tile rows
-  // (1 KB of LDS); lane l writes row l/8, physical chunk l%8, which holds the
-  // logical chunk (l%8) ^ (row & 7) = (l%8) ^ (l/8).
-  const int lrow = wave * 8 + (lane >> 3);
-  const int lchunk = (lane & 7) ^ (lane >> 3);
+  // Loader geometry: a wave's load instruction fills RPI consecutive tile
+  // rows (1 KB of LDS); lane l writes row l / CPR, physical chunk l % CPR,
+  // so it fetches the logical chunk that the swizzle puts there (its own
+  // inverse, being an XOR).
+  const int lrow = wave * RPI + lane / CPR;
+  const int lchunk = swz<CPR>(lane / CPR, lane % CPR);
+
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)x_bytes, kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, (int)w_bytes, kRawBufferFlags);
 
   RowInfo ri[A_LOADS];
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) ri[i] = decode_row(p, m0 + i * 32 + lrow);
-  const T* bsrc[B_LOADS];
+  for (int i = 0; i < A_LOADS; ++i) {
+    ri[i] = decode_row(p, m0 + i * RPR + lrow);
+    ri[i].base = (ri[i].base + lchunk * 8) * 2;   // byte offset of this lane's chunk at tap 0
+  }
+  uint32_t boff[B_LOADS];
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
-    const int n = n0 + j * 32 + lrow;
-    bsrc[j] = n < p.cout ? w + (int64_t)n * p.K + lchunk * 8 : nullptr;
+    const int n = n0 + j * RPR + lrow;
+    boff[j] = n < p.cout ? (uint32_t)((n * p.K + lchunk * 8) * 2) : kOutOfRange;
   }
-  const char* zero = (const char*)g_zero_block;
 
   const int S = (p.cin / BK) * p.ntaps;
   int ic = 0, ikd = 0, ikh = 0, ikw = 0;  // (channel chunk, tap) of the next step to issue
@@ -95,19 +143,19 @@ __global__ __launch_bounds__(256) void conv_main_kernel(ConvParams p, const T* _
   auto issue = [&](int stage) {
     char* sa = smem + stage * STAGE_BYTES;
     char* sb = sa + BM * ROWB;
-    const int xoff = ikd * p.xs_d + ikh * p.xs_h + ikw * p.xs_w + ic * BK + lchunk * 8;
+    const int xoff = (ikd * p.xs_d + ikh * p.xs_h + ikw * p.xs_w + ic * BK) * 2;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
-      const void* src =
-          tap_valid(ri[i], ikd, ikh, ikw) ? (const void*)(x + ri[i].base + xoff) : (const void*)zero;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sa + (i * 32 + wave * 8) * ROWB), 16, 0, 0);
+      const uint32_t off =
+          tap_valid(ri[i], ikd, ikh, ikw) ? (uint32_t)(ri[i].base + xoff) : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (lds_ptr_t)(sa + (i * RPR + wave * RPI) * ROWB), 16, off, 0, 0, 0);
     }
-    const int woff = ((ikd * p.kh + ikh) * p.kw + ikw) * p.cin + ic * BK;
+    const uint32_t woff = (uint32_t)((((ikd * p.kh + ikh) * p.kw + ikw) * p.cin + ic * BK) * 2);
 #pragma unroll
-    for (int j = 0; j < B_LOADS; ++j) {
-      const void* src = bsrc[j] ? (const void*)(bsrc[j] + woff) : (const void*)zero;
-      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(sb + (j * 32 + wave * 8) * ROWB), 16, 0, 0);
-    }
+    for (int j = 0; j < B_LOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wr, (lds_ptr_t)(sb + (j * RPR + wave * RPI) * ROWB), 16, boff[j] + woff, 0, 0, 0);
     if (++ikw == p.kw) {
       ikw = 0;
       if (++ikh == p.kh) {
@@ -120,14 +168,16 @@ __global__ __launch_bounds__(256) void conv_main_kernel(ConvParams p, const T* _
     }
   };
 
-  f32x4_t acc[FM][FN];
+  AccT acc[FM][FN];
 #pragma unroll
   for (int a = 0; a < FM; ++a)
 #pragma unroll
-    for (int b = 0; b < FN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < FN; ++b)
+#pragma unroll
+      for (int e = 0; e < NACC; ++e) acc[a][b][e] = 0.f;
 
   const int wm = wave / WN, wn = wave % WN;
-  const int fr = lane & 15, fg = lane >> 4;
+  const int fr = lane % MF, fg = lane / MF;   // fragment row, k group
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
@@ -144,66 +194,110 @@ __global__ __launch_bounds__(256) void conv_main_kernel(ConvParams p, const T* _
     const char* sa = smem + (s % STAGES) * STAGE_BYTES;
     const char* sb = sa + BM * ROWB;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int chunk = ((ks * 4 + fg) ^ (fr & 7)) * 16;
+    for (int ks = 0; ks < BK / KSUB; ++ks) {
+      const int chunk = swz<CPR>(fr, ks * LG + fg) * 16;
       V8 af[FM], bfr[FN];
 #pragma unroll
       for (int a = 0; a < FM; ++a)
-        af[a] = *(const V8*)(sa + (wm * TM + a * 16 + fr) * ROWB + chunk);
+        af[a] = *(const V8*)(sa + (wm * TM + a * MF + fr) * ROWB + chunk);
 #pragma unroll
       for (int b = 0; b < FN; ++b)
-        bfr[b] = *(const V8*)(sb + (wn * TN + b * 16 + fr) * ROWB + chunk);
+        bfr[b] = *(const V8*)(sb + (wn * TN + b * MF + fr) * ROWB + chunk);
 #pragma unroll
       for (int a = 0; a < FM; ++a)
 #pragma unroll
-        for (int b = 0; b < FN; ++b) acc[a][b] = mfma16x16x32(bfr[b], af[a], acc[a][b]);
+        for (int b = 0; b < FN; ++b) acc[a][b] = mfma_block(bfr[b], af[a], acc[a][b]);
     }
   }
 
-  // Epilogue: lane holds D[n = 4*fg + i][m = fr] of each 16x16 block.
+  // Epilogue: for output row m = its fragment row, a lane holds runs of 4
+  // consecutive output channels: channel 16*b' + 4*fg + i (MF = 16) or
+  // 32*b' + 8*q + 4*fg + i (MF = 32, q = 0..3) in accumulator element 4*q + i.
 #pragma unroll
   for (int a = 0; a < FM; ++a) {
-    const int m = m0 + wm * TM + a * 16 + fr;
+    const int m = m0 + wm * TM + a * MF + fr;
     if (m >= p.M) continue;
     T* yrow = y + (int64_t)m * p.cout;
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
-      const int n = n0 + wn * TN + b * 16 + fg * 4;
-      if (n + 3 < p.cout) {
-        union { T h[4]; uint2 u; } pk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[a][b][i]);
-        *(uint2*)(yrow + n) = pk.u;
-      } else {
+      for (int q = 0; q < NQ; ++q) {
+        const int n = n0 + wn * TN + b * MF + 8 * q + 4 * fg;
+        if (n + 3 < p.cout) {
+          union { T h[4]; uint2 u; } pk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (n + i < p.cout) yrow[n + i] = from_f32<T>(acc[a][b][i]);
+          for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[a][b][4 * q + i]);
+          *(uint2*)(yrow + n) = pk.u;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (n + i < p.cout) yrow[n + i] = from_f32<T>(acc[a][b][4 * q + i]);
+        }
       }
     }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int STAGES>
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int MF>
 hipError_t launch_cfg(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.cout + BN - 1) / BN;
-  hipLaunchKernelGGL((conv_main_kernel<T, BM, BN, WM, WN, STAGES>), dim3(tiles_m * tiles_n),
-                     dim3(256), 0, s, p, (const T*)x, (const T*)w, (T*)y, tiles_n);
+  const uint32_t xb = (uint32_t)((int64_t)p.n * p.xs_n * 2);
+  const uint32_t wb = (uint32_t)((int64_t)p.cout * p.K * 2);
+  hipLaunchKernelGGL((conv_main_kernel<T, BM, BN, BK, WM, WN, STAGES, OCC, MF>),
+                     dim3(tiles_m * tiles_n), dim3(256), 0, s, p, (const T*)x, (const T*)w,
+                     (T*)y, tiles_n, xb, wb);
   return hipGetLastError();
+}
+
+// Tile configurations.  CONVFWD_MAIN_VARIANT (a build-time define) forces one
+// of them for every problem, for tile-size sweeps; by default the choice below
+// depends on the problem size and channel alignment.
+constexpr int variant_bk(int v) {
+  return (v == 1 || v == 4 || v == 7 || v == 41 || v == 43 || v == 45 || v == 47) ? 64 : 32;
+}
+
+template <typename T>
+hipError_t launch_variant(int v, const ConvParams& p, const void* x, const void* w, void* y,
+                          hipStream_t s) {
+  switch (v) {
+    // 16x16x32 MFMA blocks
+    case 1: return launch_cfg<T, 256, 128, 64, 4, 1, 3, 1, 16>(p, x, w, y, s);
+    case 3: return launch_cfg<T, 256, 128, 32, 4, 1, 2, 2, 16>(p, x, w, y, s);
+    case 4: return launch_cfg<T, 128, 128, 64, 2, 2, 2, 2, 16>(p, x, w, y, s);
+    case 7: return launch_cfg<T, 64, 128, 64, 1, 4, 3, 2, 16>(p, x, w, y, s);
+    case 8: return launch_cfg<T, 128, 64, 32, 2, 2, 3, 2, 16>(p, x, w, y, s);
+    // 32x32x16 MFMA blocks
+    case 41: return launch_cfg<T, 256, 128, 64, 4, 1, 2, 1, 32>(p, x, w, y, s);
+    case 42: return launch_cfg<T, 256, 128, 32, 4, 1, 2, 2, 32>(p, x, w, y, s);
+    case 43: return launch_cfg<T, 128, 128, 64, 2, 2, 2, 2, 32>(p, x, w, y, s);
+    case 44: return launch_cfg<T, 256, 128, 32, 4, 1, 3, 2, 32>(p, x, w, y, s);
+    case 45: return launch_cfg<T, 256, 128, 64, 4, 1, 3, 1, 32>(p, x, w, y, s);
+    case 46: return launch_cfg<T, 256, 128, 32, 2, 2, 2, 2, 32>(p, x, w, y, s);
+    case 47: return launch_cfg<T, 128, 128, 64, 2, 2, 3, 1, 32>(p, x, w, y, s);
+    case 48: return launch_cfg<T, 128, 128, 32, 2, 2, 3, 2, 32>(p, x, w, y, s);
+    case 49: return launch_cfg<T, 128, 64, 32, 2, 2, 3, 2, 32>(p, x, w, y, s);
+    default: return launch_cfg<T, 128, 64, 32, 2, 2, 3, 2, 16>(p, x, w, y, s);
+  }
 }
 
 template <typename T>
 hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
-  // Enough 256-row tiles to fill 256 CUs: big tiles; otherwise smaller ones.
+#ifdef CONVFWD_MAIN_VARIANT
+  if (p.cin % variant_bk(CONVFWD_MAIN_VARIANT) == 0)
+    return launch_variant<T>(CONVFWD_MAIN_VARIANT, p, x, w, y, s);
+#endif
+  const bool bk64 = p.cin % 64 == 0;
   const long tiles_256 = (long)((p.M + 255) / 256) * ((p.cout + 127) / 128);
-  if (tiles_256 >= 256) return launch_cfg<T, 256, 128, 4, 1, 3>(p, x, w, y, s);
-  return launch_cfg<T, 128, 64, 2, 2, 3>(p, x, w, y, s);
+  if (tiles_256 >= 256) return launch_variant<T>(bk64 ? 4 : 3, p, x, w, y, s);
+  return launch_variant<T>(bk64 ? 7 : 8, p, x, w, y, s);
 }
 
 }  // namespace
 
 bool main_accepts(const ConvParams& p, int dtype) {
-  return (dtype == kF16 || dtype == kBF16) && p.cin % 64 == 0 && p.cout % 4 == 0 && p.kd <= 16 &&
+  return (dtype == kF16 || dtype == kBF16) && p.cin % 32 == 0 && p.cout % 4 == 0 && p.kd <= 16 &&
          p.kh <= 16 && p.kw <= 16;
 }
 

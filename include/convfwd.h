@@ -68,13 +68,17 @@ enum {
  * testing every path on every shape it accepts). */
 typedef enum {
   CONVFWD_PATH_AUTO = 0,
-  CONVFWD_PATH_MAIN = 1,   /* fp16/bf16, C_in % 64 == 0, C_out % 4 == 0, filter <= 16 per dim:
+  CONVFWD_PATH_MAIN = 1,   /* fp16/bf16, C_in % 32 == 0, C_out % 4 == 0, filter <= 16 per dim:
                               16-byte channels-last loads straight into LDS, MFMA */
   CONVFWD_PATH_FLATK = 2,  /* any C_in (the unaligned-channel tail path), filter <= 16 per dim:
                               element-granular gathers over the flattened (tap, channel) axis, MFMA */
   CONVFWD_PATH_ROWS = 3,   /* fp16/bf16 tiny C_in (C_in * K_w <= 64, 2D or 3D): whole input rows
                               staged in LDS, MFMA */
-  CONVFWD_PATH_DIRECT = 4  /* any problem: one thread per output, fp32 FMA (slow, simple) */
+  CONVFWD_PATH_DIRECT = 4, /* any problem: one thread per output, fp32 FMA (slow, simple) */
+  CONVFWD_PATH_BRICK = 5   /* fp16/bf16, C_in % 16 == 0, C_out % 4 == 0, >= 3 taps, filter <= 16
+                              per dim and a brick that fits: the input brick of a box of up to
+                              512 outputs staged in LDS per 16-channel chunk, every tap read
+                              from it, MFMA */
 } convfwd_path;
 
 /* Problem descriptor.  All extents in elements. */
@@ -111,7 +115,7 @@ int conv_fwd_path(const convfwd_desc* desc, int path, const void* x, const void*
 /* Static message for a return code; never NULL. */
 const char* conv_strerror(int code);
 
-/* Static name of a path ("main", "flatk", "rows", "direct", "auto"); never NULL. */
+/* Static name of a path ("auto", "main", "flatk", "rows", "direct", "brick"); never NULL. */
 const char* conv_path_name(int path);
 
 #ifdef __cplusplus

@@ -114,7 +114,7 @@ def test_empty_batch_is_a_no_op():
 
 def test_forced_path_rules():
     lib = igc.lib()
-    # main path needs C_in % 64 == 0 and fp16/bf16
+    # main path needs C_in % 32 == 0 and fp16/bf16
     d = _desc(c_in=65, n=0)
     assert lib.conv_fwd_path(ctypes.byref(d), 1, None, None, None, None) == -3
     d = _desc(c_in=64, dtype=0, n=0)
@@ -132,20 +132,20 @@ def test_strerror_and_path_names():
     lib = igc.lib()
     for code in range(-7, 1):
         assert lib.conv_strerror(code)
-    assert [lib.conv_path_name(i).decode() for i in range(5)] == ["auto", "main", "flatk", "rows",
-                                                                  "direct"]
+    assert [lib.conv_path_name(i).decode() for i in range(6)] == ["auto", "main", "flatk", "rows",
+                                                                  "direct", "brick"]
 
 
 EXPECTED_PATHS = {
     "c1_conv3d_fp32_n1_8c16_o32": "flatk",
-    "c2_conv2d_fp16_n32_56c256_o256": "main",
-    "c4a_conv3d_fp16_n4_32c128_o128": "main",
-    "c4b_conv3d_fp16_n1_64c64_o128": "main",
+    "c2_conv2d_fp16_n32_56c256_o256": "brick",
+    "c4a_conv3d_fp16_n4_32c128_o128": "brick",
+    "c4b_conv3d_fp16_n1_64c64_o128": "brick",
     "c4c_conv3d_fp16_n4_32c64_o128_s2": "main",
     "c5a_conv3d_bf16_n4_32c65_o65": "flatk",
     "c5b_conv3d_bf16_n4_16c21_o21": "flatk",
-    "c5c_conv3d_bf16_n4_32c64_o128_k311": "main",
-    "c5d_conv3d_bf16_n4_32c64_o128_k133": "main",
+    "c5c_conv3d_bf16_n4_32c64_o128_k311": "brick",
+    "c5d_conv3d_bf16_n4_32c64_o128_k133": "brick",
 }
 
 

@@ -49,12 +49,16 @@ CASES = [
     _case("bf16_c1_single_output", "bf16", (1, 3, 3, 1), (1, 3, 3, 1), (1, 1), (0, 0), seed=17),
     _case("fp16_1x1_pointwise", "fp16", (2, 5, 7, 64), (64, 1, 1, 64), (1, 1), (0, 0), seed=18),
 ]
-PATHS = ["main", "flatk", "direct"]
+PATHS = ["main", "brick", "flatk", "direct"]
 
 
 def _accepts(wl, path):
+    half = wl.dtype in ("fp16", "bf16") and wl.w_shape[0] % 4 == 0
+    taps = int(np.prod(wl.w_shape[1:-1]))
     if path == "main":
-        return wl.dtype in ("fp16", "bf16") and wl.x_shape[-1] % 64 == 0 and wl.w_shape[0] % 4 == 0
+        return half and wl.x_shape[-1] % 32 == 0
+    if path == "brick":
+        return half and wl.x_shape[-1] % 16 == 0 and taps >= 3
     return True
 
 
@@ -113,6 +117,9 @@ def test_parity_full_size_sampled(name):
 
 EXACT = [
     ("main", "fp16", (2, 5, 6, 7, 64), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
+    ("brick", "fp16", (2, 5, 6, 7, 64), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
+    ("brick", "bf16", (1, 6, 7, 9, 32), (3, 3, 3), (2, 2, 2), (2, 1, 3)),
+    ("brick", "fp16", (2, 3, 9, 40, 16), (1, 5, 3), (1, 1, 2), (0, 2, 1)),
     ("main", "bf16", (1, 6, 7, 9, 64), (3, 3, 3), (2, 2, 2), (2, 1, 3)),
     ("flatk", "bf16", (2, 5, 6, 7, 5), (3, 3, 3), (1, 2, 1), (1, 1, 2)),
     ("flatk", "fp32", (1, 4, 9, 8, 3), (1, 7, 7), (1, 2, 2), (0, 3, 3)),
