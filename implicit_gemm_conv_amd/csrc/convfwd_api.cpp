@@ -79,9 +79,9 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
   return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
 }
 
+// The brick path is available on request; on the measured shapes the
+// per-tap-gather main path is faster, so AUTO does not pick it.
 int auto_path(const ConvParams& p, int dtype) {
-  const bool unit_stride = p.sd == 1 && p.sh == 1 && p.sw == 1;
-  if (unit_stride && convfwd::brick_accepts(p, dtype)) return CONVFWD_PATH_BRICK;
   if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;
   if (convfwd::flatk_accepts(p, dtype)) return CONVFWD_PATH_FLATK;

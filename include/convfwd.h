@@ -75,7 +75,7 @@ typedef enum {
   CONVFWD_PATH_ROWS = 3,   /* fp16/bf16 tiny C_in (C_in * K_w <= 64, 2D or 3D): whole input rows
                               staged in LDS, MFMA */
   CONVFWD_PATH_DIRECT = 4, /* any problem: one thread per output, fp32 FMA (slow, simple) */
-  CONVFWD_PATH_BRICK = 5   /* fp16/bf16, C_in % 16 == 0, C_out % 4 == 0, >= 3 taps, filter <= 16
+  CONVFWD_PATH_BRICK = 5   /* fp16/bf16, C_in % 16 == 0, C_out % 4 == 0, >= 4 taps, filter <= 16
                               per dim and a brick that fits: the input brick of a box of up to
                               512 outputs staged in LDS per 16-channel chunk, every tap read
                               from it, MFMA */

@@ -138,14 +138,14 @@ def test_strerror_and_path_names():
 
 EXPECTED_PATHS = {
     "c1_conv3d_fp32_n1_8c16_o32": "flatk",
-    "c2_conv2d_fp16_n32_56c256_o256": "brick",
-    "c4a_conv3d_fp16_n4_32c128_o128": "brick",
-    "c4b_conv3d_fp16_n1_64c64_o128": "brick",
+    "c2_conv2d_fp16_n32_56c256_o256": "main",
+    "c4a_conv3d_fp16_n4_32c128_o128": "main",
+    "c4b_conv3d_fp16_n1_64c64_o128": "main",
     "c4c_conv3d_fp16_n4_32c64_o128_s2": "main",
     "c5a_conv3d_bf16_n4_32c65_o65": "flatk",
     "c5b_conv3d_bf16_n4_16c21_o21": "flatk",
-    "c5c_conv3d_bf16_n4_32c64_o128_k311": "brick",
-    "c5d_conv3d_bf16_n4_32c64_o128_k133": "brick",
+    "c5c_conv3d_bf16_n4_32c64_o128_k311": "main",
+    "c5d_conv3d_bf16_n4_32c64_o128_k133": "main",
 }
 
 

@@ -58,7 +58,7 @@ def _accepts(wl, path):
     if path == "main":
         return half and wl.x_shape[-1] % 32 == 0
     if path == "brick":
-        return half and wl.x_shape[-1] % 16 == 0 and taps >= 3
+        return half and wl.x_shape[-1] % 16 == 0 and taps >= 4
     return True
 
 
