@@ -16,8 +16,10 @@ The JSON line also carries
                 on this host's cores, rank 0 only.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,6 +35,45 @@ from conv_workloads import HEADLINE, WORKLOADS, make_inputs  # noqa: E402
 
 PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}   # MI355X dense, published
 METRIC = "conv fwd TFLOP/s (2·M·N·K) and % of MFMA peak, fp16 NDHWC 3×3×3 shapes"
+DOMINANT = "conv_main_kernel<fp16, BM=128, BN=128, BK=64, 16x16x32 MFMA> (c4a, c4b)"
+# Sources whose hash the stored counter figures are tied to.
+KERNEL_SOURCES = ["implicit_gemm_conv_amd/csrc/k_main.hip", "implicit_gemm_conv_amd/csrc/conv_device.h",
+                  "implicit_gemm_conv_amd/csrc/conv_params.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_main_fp16_c4ab_hbm_traffic.md")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+    or None when it is missing or was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def copy_calibration(mib=512, reps=5):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib * 2**20 // 2
+    a = torch.randn(n, device="cuda:0", dtype=torch.float32).to(torch.float16)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n * 2, "bytes_written_per_copy": n * 2,
+                                           "copies": reps}}), flush=True)
 
 
 def gemm_dims(wl):
@@ -81,6 +122,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=1.0,
                     help="share of one step's output rows the CPU oracle computes")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -91,6 +134,9 @@ def main():
         sys.exit(2)
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     wls = [WORKLOADS[n] for n in HEADLINE]
     inputs = [make_inputs(wl, dev) for wl in wls]
     outs = [torch.empty(igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding),
@@ -142,11 +188,15 @@ def main():
                             for s in range(args.steps) for i in dom]))
     dom_flops = flops[0]
     achieved = dom_flops / (dom_us * 1e-6) / 1e12
+    alg_bytes = [2 * (int(np.prod(wl.x_shape)) + int(np.prod(wl.w_shape)) +
+                      int(np.prod(igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding))))
+                 for wl in wls]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp16"],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp16"], 4),
-                "traffic": None,
-                "kernel": "conv_main_kernel<fp16, BM=256, BN=128> (c4a, c4b)",
-                "launch_us": round(dom_us, 3), "flops_per_launch": dom_flops}
+                "traffic": stored_traffic(),
+                "kernel": DOMINANT, "kernel_source_sha256": kernel_source_hash(),
+                "launch_us": round(dom_us, 3), "flops_per_launch": dom_flops,
+                "algorithmic_bytes_per_launch": float(np.mean([alg_bytes[i] for i in dom]))}
 
     value = step_flops * args.steps / (total_ms * 1e-3) / 1e12
     rec = {

@@ -146,6 +146,7 @@ EXPECTED_PATHS = {
     "c5b_conv3d_bf16_n4_16c21_o21": "flatk",
     "c5c_conv3d_bf16_n4_32c64_o128_k311": "main",
     "c5d_conv3d_bf16_n4_32c64_o128_k133": "main",
+    "c3_conv2d_fp16_stem_n64_224c3_o64_k7s2": "rows",
 }
 
 

@@ -42,14 +42,16 @@ CASES = [
     _case("bf16_2d_k5", "bf16", (2, 12, 13, 64), (32, 5, 5, 64), (1, 1), (2, 2), seed=10),
     _case("c5a_like_bf16_c65", "bf16", (2, 7, 8, 9, 65), (65, 3, 3, 3, 65), (1, 1, 1), (1, 1, 1), seed=11),
     _case("c5b_like_bf16_c21", "bf16", (3, 6, 7, 8, 21), (21, 3, 3, 3, 21), (1, 1, 1), (1, 1, 1), seed=12),
-    _case("c3_like_fp16_stem", "fp16", (2, 30, 31, 3), (64, 7, 7, 3), (2, 2), (3, 3), "normal", seed=13),
+    _case("c3_like_fp16_stem", "fp16", (2, 30, 32, 3), (64, 7, 7, 3), (2, 2), (3, 3), "normal", seed=13),
+    _case("stem_wide_ragged_bf16", "bf16", (1, 11, 240, 3), (40, 7, 7, 3), (2, 2), (3, 3), "normal", seed=19),
+    _case("tiny_c3_3d_fp16", "fp16", (2, 5, 9, 8, 3), (32, 3, 3, 3, 3), (1, 1, 1), (1, 1, 1), seed=20),
     _case("c1_fp32", "fp32", (1, 8, 8, 8, 16), (32, 3, 3, 3, 16), (1, 1, 1), (1, 1, 1), seed=14),
     _case("fp32_odd", "fp32", (2, 5, 6, 7, 5), (7, 3, 2, 3, 5), (1, 2, 1), (1, 0, 2), seed=15),
     _case("fp16_c16", "fp16", (2, 6, 6, 6, 16), (32, 3, 3, 3, 16), (1, 1, 1), (1, 1, 1), seed=16),
     _case("bf16_c1_single_output", "bf16", (1, 3, 3, 1), (1, 3, 3, 1), (1, 1), (0, 0), seed=17),
     _case("fp16_1x1_pointwise", "fp16", (2, 5, 7, 64), (64, 1, 1, 64), (1, 1), (0, 0), seed=18),
 ]
-PATHS = ["main", "brick", "flatk", "direct"]
+PATHS = ["main", "brick", "rows", "flatk", "direct"]
 
 
 def _accepts(wl, path):
@@ -59,6 +61,10 @@ def _accepts(wl, path):
         return half and wl.x_shape[-1] % 32 == 0
     if path == "brick":
         return half and wl.x_shape[-1] % 16 == 0 and taps >= 4
+    if path == "rows":
+        cin, kw = wl.x_shape[-1], wl.w_shape[-2]
+        return (wl.dtype in ("fp16", "bf16") and cin < 16 and cin * kw <= 32
+                and wl.w_shape[0] <= 64 and (wl.x_shape[-2] * cin) % 8 == 0)
     return True
 
 
@@ -125,6 +131,8 @@ EXACT = [
     ("flatk", "fp32", (1, 4, 9, 8, 3), (1, 7, 7), (1, 2, 2), (0, 3, 3)),
     ("flatk", "fp16", (2, 5, 6, 7, 65), (3, 3, 3), (3, 1, 2), (3, 1, 0)),
     ("direct", "fp16", (1, 5, 6, 7, 3), (3, 3, 3), (2, 2, 2), (1, 1, 1)),
+    ("rows", "fp16", (1, 1, 19, 16, 3), (1, 7, 7), (1, 2, 2), (0, 3, 3)),
+    ("rows", "bf16", (2, 5, 9, 8, 3), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
 ]
 
 
