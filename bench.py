@@ -8,7 +8,8 @@ launch of the library's auto path on the current stream.  The metric is
 the timed steps, in TFLOP/s.
 
 The JSON line also carries
-  roofline:     the dominant kernel (the one running the two 116-GFLOP
+  roofline:     the dominant kernel (the path with the largest share of the
+                step; the strip kernel runs both unit-stride 116-GFLOP
                 convolutions) timed launch by launch with HIP events on the
                 launch stream, against the MI355X dense fp16 MFMA peak;
   cpu_baseline: the float64 CPU oracle on a bounded sample of the same
@@ -35,30 +36,38 @@ from conv_workloads import HEADLINE, WORKLOADS, make_inputs  # noqa: E402
 
 PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}   # MI355X dense, published
 METRIC = "conv fwd TFLOP/s (2·M·N·K) and % of MFMA peak, fp16 NDHWC 3×3×3 shapes"
-DOMINANT = "conv_main_kernel<fp16, BM=128, BN=128, BK=64, 16x16x32 MFMA> (c4a, c4b)"
-# Sources whose hash the stored counter figures are tied to.
-KERNEL_SOURCES = ["implicit_gemm_conv_amd/csrc/k_main.hip", "implicit_gemm_conv_amd/csrc/conv_device.h",
-                  "implicit_gemm_conv_amd/csrc/conv_params.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_main_fp16_c4ab_hbm_traffic.md")
+# Per path: the kernel it launches on these shapes and the sources that kernel is built from
+# (the stored counter figures are tied to their hash).
+_COMMON = ["implicit_gemm_conv_amd/csrc/conv_device.h", "implicit_gemm_conv_amd/csrc/conv_params.h"]
+KERNELS = {
+    "strip": ("conv_strip_kernel<fp16, K_w=3>: 512x128 tile, 32x32x16 MFMA",
+              ["implicit_gemm_conv_amd/csrc/k_strip.hip", *_COMMON]),
+    "main": ("conv_main_kernel<fp16>: 128x128 tile, BK=64, 16x16x32 MFMA",
+             ["implicit_gemm_conv_amd/csrc/k_main.hip", *_COMMON]),
+}
 
 
-def kernel_source_hash():
+def traffic_file(path):
+    return os.path.join(ROOT, "profiles", f"conv_{path}_fp16_c4ab_hbm_traffic.md")
+
+
+def kernel_source_hash(path="strip"):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNELS[path][1]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter summary,
+def stored_traffic(path):
+    """HBM bytes per launch of the path's kernel from the committed counter summary,
     or None when it is missing or was taken on other kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if path not in KERNELS or not os.path.exists(traffic_file(path)):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(traffic_file(path)).read()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash():
+    if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash(path):
         return None
     return float(m_bytes.group(1))
 
@@ -85,8 +94,7 @@ def gemm_dims(wl):
 
 
 def kernel_key(wl):
-    """Kernels are identified by path + tile choice; the two unit-stride 116-GFLOP
-    convolutions share one kernel instantiation."""
+    """The path AUTO takes; on these shapes a path launches one kernel instantiation."""
     return igc.select_path(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.torch_dtype)
 
 
@@ -182,19 +190,24 @@ def main():
                         "tflops": round(flops[i] / (us * 1e-6) / 1e12, 2),
                         "pct_peak": round(100 * flops[i] / (us * 1e-6) / 1e12 / PEAK_TFLOPS["fp16"], 2)}
 
-    # Dominant kernel: the one running the two unit-stride 116-GFLOP convolutions.
-    dom = [0, 1]
+    # Dominant kernel: the path with the largest summed launch time over the step.
+    keys = [kernel_key(wl) for wl in wls]
+    share = {k: sum(per[wl.name]["us_mean"] for wl, kk in zip(wls, keys) if kk == k) for k in set(keys)}
+    dom_path = max(share, key=share.get)
+    dom = [i for i, k in enumerate(keys) if k == dom_path]
     dom_us = float(np.mean([1e3 * ev[s][i][0].elapsed_time(ev[s][i][1])
                             for s in range(args.steps) for i in dom]))
-    dom_flops = flops[0]
+    dom_flops = float(np.mean([flops[i] for i in dom]))
     achieved = dom_flops / (dom_us * 1e-6) / 1e12
     alg_bytes = [2 * (int(np.prod(wl.x_shape)) + int(np.prod(wl.w_shape)) +
                       int(np.prod(igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding))))
                  for wl in wls]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp16"],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp16"], 4),
-                "traffic": stored_traffic(),
-                "kernel": DOMINANT, "kernel_source_sha256": kernel_source_hash(),
+                "traffic": stored_traffic(dom_path),
+                "kernel": KERNELS.get(dom_path, (dom_path,))[0] + " (" +
+                          ", ".join(wls[i].name.split("_")[0] for i in dom) + ")",
+                "kernel_source_sha256": kernel_source_hash(dom_path) if dom_path in KERNELS else None,
                 "launch_us": round(dom_us, 3), "flops_per_launch": dom_flops,
                 "algorithmic_bytes_per_launch": float(np.mean([alg_bytes[i] for i in dom]))}
 

@@ -37,11 +37,14 @@ hipError_t launch_rows(const ConvParams& p, int dtype, const void* x, const void
                        hipStream_t s);
 hipError_t launch_brick(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
                         hipStream_t s);
+hipError_t launch_strip(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                        hipStream_t s);
 
 // Whether a path accepts a problem (host-side rules mirrored in convfwd.h).
 bool main_accepts(const ConvParams& p, int dtype);
 bool flatk_accepts(const ConvParams& p, int dtype);
 bool rows_accepts(const ConvParams& p, int dtype);
 bool brick_accepts(const ConvParams& p, int dtype);
+bool strip_accepts(const ConvParams& p, int dtype);
 
 }  // namespace convfwd

@@ -82,6 +82,9 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
 // The brick path is available on request; on the measured shapes the
 // per-tap-gather main path is faster, so AUTO does not pick it.
 int auto_path(const ConvParams& p, int dtype) {
+  // The strip path wins once the w-taps share a strip (K_w >= 2); with K_w = 1
+  // it is the main path with a larger tile and the main path is faster.
+  if (p.kw >= 2 && convfwd::strip_accepts(p, dtype)) return CONVFWD_PATH_STRIP;
   if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;
   if (convfwd::flatk_accepts(p, dtype)) return CONVFWD_PATH_FLATK;
@@ -95,6 +98,7 @@ bool path_accepts(int path, const ConvParams& p, int dtype) {
     case CONVFWD_PATH_ROWS: return convfwd::rows_accepts(p, dtype);
     case CONVFWD_PATH_DIRECT: return true;
     case CONVFWD_PATH_BRICK: return convfwd::brick_accepts(p, dtype);
+    case CONVFWD_PATH_STRIP: return convfwd::strip_accepts(p, dtype);
     default: return false;
   }
 }
@@ -116,6 +120,7 @@ int run(const convfwd_desc* desc, int path, const void* x, const void* w, void* 
     case CONVFWD_PATH_FLATK: e = convfwd::launch_flatk(p, desc->dtype, x, w, y, s); break;
     case CONVFWD_PATH_ROWS: e = convfwd::launch_rows(p, desc->dtype, x, w, y, s); break;
     case CONVFWD_PATH_BRICK: e = convfwd::launch_brick(p, desc->dtype, x, w, y, s); break;
+    case CONVFWD_PATH_STRIP: e = convfwd::launch_strip(p, desc->dtype, x, w, y, s); break;
     default: e = convfwd::launch_direct(p, desc->dtype, x, w, y, s); break;
   }
   if (e != hipSuccess) return CONVFWD_ERR_LAUNCH;
@@ -150,7 +155,7 @@ int conv_fwd(const convfwd_desc* desc, const void* x, const void* w, void* y, vo
 
 int conv_fwd_path(const convfwd_desc* desc, int path, const void* x, const void* w, void* y,
                   void* stream) {
-  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_BRICK) return CONVFWD_ERR_UNSUPPORTED;
+  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_STRIP) return CONVFWD_ERR_UNSUPPORTED;
   return run(desc, path, x, w, y, stream);
 }
 
@@ -175,6 +180,7 @@ const char* conv_path_name(int path) {
     case CONVFWD_PATH_ROWS: return "rows";
     case CONVFWD_PATH_DIRECT: return "direct";
     case CONVFWD_PATH_BRICK: return "brick";
+    case CONVFWD_PATH_STRIP: return "strip";
     default: return "unknown";
   }
 }

@@ -75,10 +75,14 @@ typedef enum {
   CONVFWD_PATH_ROWS = 3,   /* fp16/bf16 tiny C_in (C_in * K_w <= 64, 2D or 3D): whole input rows
                               staged in LDS, MFMA */
   CONVFWD_PATH_DIRECT = 4, /* any problem: one thread per output, fp32 FMA (slow, simple) */
-  CONVFWD_PATH_BRICK = 5   /* fp16/bf16, C_in % 16 == 0, C_out % 4 == 0, >= 4 taps, filter <= 16
+  CONVFWD_PATH_BRICK = 5,  /* fp16/bf16, C_in % 16 == 0, C_out % 4 == 0, >= 4 taps, filter <= 16
                               per dim and a brick that fits: the input brick of a box of up to
                               512 outputs staged in LDS per 16-channel chunk, every tap read
                               from it, MFMA */
+  CONVFWD_PATH_STRIP = 6   /* fp16/bf16, C_in % 32 == 0, C_out % 4 == 0, stride 1 along w,
+                              W_out % 32 == 0, K_w <= 5, K_d, K_h <= 16: per (channel chunk,
+                              kd, kh) one input strip per 32-output w-segment staged in LDS,
+                              all K_w taps read from it, 512 x 128 tiles, MFMA */
 } convfwd_path;
 
 /* Problem descriptor.  All extents in elements. */
@@ -115,7 +119,8 @@ int conv_fwd_path(const convfwd_desc* desc, int path, const void* x, const void*
 /* Static message for a return code; never NULL. */
 const char* conv_strerror(int code);
 
-/* Static name of a path ("auto", "main", "flatk", "rows", "direct", "brick"); never NULL. */
+/* Static name of a path ("auto", "main", "flatk", "rows", "direct", "brick", "strip");
+ * never NULL. */
 const char* conv_path_name(int path);
 
 #ifdef __cplusplus

@@ -50,8 +50,12 @@ CASES = [
     _case("fp16_c16", "fp16", (2, 6, 6, 6, 16), (32, 3, 3, 3, 16), (1, 1, 1), (1, 1, 1), seed=16),
     _case("bf16_c1_single_output", "bf16", (1, 3, 3, 1), (1, 3, 3, 1), (1, 1), (0, 0), seed=17),
     _case("fp16_1x1_pointwise", "fp16", (2, 5, 7, 64), (64, 1, 1, 64), (1, 1), (0, 0), seed=18),
+    _case("strip_fp16_c64_w32", "fp16", (2, 5, 6, 32, 64), (128, 3, 3, 3, 64), (1, 1, 1), (1, 1, 1), seed=21),
+    _case("strip_bf16_c96_w64_o72", "bf16", (1, 4, 5, 64, 96), (72, 3, 3, 3, 96), (1, 1, 1), (1, 1, 1), seed=22),
+    _case("strip_fp16_2d_k5_o132", "fp16", (3, 9, 32, 32), (132, 5, 5, 32), (1, 1), (1, 2), seed=23),
+    _case("strip_fp16_hs2_w32", "fp16", (2, 7, 9, 34, 64), (64, 3, 3, 3, 64), (2, 2, 1), (1, 0, 0), seed=24),
 ]
-PATHS = ["main", "brick", "rows", "flatk", "direct"]
+PATHS = ["strip", "main", "brick", "rows", "flatk", "direct"]
 
 
 def _accepts(wl, path):
@@ -59,6 +63,10 @@ def _accepts(wl, path):
     taps = int(np.prod(wl.w_shape[1:-1]))
     if path == "main":
         return half and wl.x_shape[-1] % 32 == 0
+    if path == "strip":
+        ow = (wl.x_shape[-2] + 2 * wl.padding[-1] - wl.w_shape[-2]) // wl.stride[-1] + 1
+        return (half and wl.x_shape[-1] % 32 == 0 and wl.stride[-1] == 1 and ow % 32 == 0
+                and wl.w_shape[-2] <= 5)
     if path == "brick":
         return half and wl.x_shape[-1] % 16 == 0 and taps >= 4
     if path == "rows":
@@ -123,6 +131,8 @@ def test_parity_full_size_sampled(name):
 
 EXACT = [
     ("main", "fp16", (2, 5, 6, 7, 64), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
+    ("strip", "fp16", (2, 5, 6, 32, 64), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
+    ("strip", "bf16", (1, 6, 7, 33, 32), (3, 2, 2), (2, 2, 1), (2, 1, 0)),
     ("brick", "fp16", (2, 5, 6, 7, 64), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
     ("brick", "bf16", (1, 6, 7, 9, 32), (3, 3, 3), (2, 2, 2), (2, 1, 3)),
     ("brick", "fp16", (2, 3, 9, 40, 16), (1, 5, 3), (1, 1, 2), (0, 2, 1)),
