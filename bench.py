@@ -15,6 +15,12 @@ The JSON line also carries
   cpu_baseline: the float64 CPU oracle on a bounded sample of the same
                 workload (a fixed set of output rows of the first convolution),
                 on this host's cores, rank 0 only.
+
+``--sweep`` instead times every workload shape on its own (10 warm-ups, then
+``--launches`` launches each between two HIP events on the launch stream;
+median and min), once with resident buffers and once "cold", rotating enough
+(x, y) buffer sets (> 512 MB) that the 256 MB MALL cannot hold them; one JSON
+line per workload.
 """
 import argparse
 import hashlib
@@ -122,6 +128,53 @@ def cpu_baseline(wls, inputs, fraction):
                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
 
 
+def sweep(launches, names=None):
+    """Per-workload event timing, warm (resident buffers) and cold (rotated buffer sets)."""
+    dev = "cuda:0"
+    stream = torch.cuda.current_stream()
+    for name, wl in WORKLOADS.items():
+        if names and name not in names:
+            continue
+        x, w = make_inputs(wl, dev)
+        shape = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding)
+        y = torch.empty(shape, dtype=wl.torch_dtype, device=dev)
+        m, n, k = gemm_dims(wl)
+        flops = 2.0 * m * n * k
+        esz = x.element_size()
+        alg_bytes = esz * (x.numel() + w.numel() + y.numel())
+        # cold: enough (x, y) sets that together they exceed 512 MB, at least 3
+        sets = max(3, -(-(512 << 20) // (esz * (x.numel() + y.numel()))) + 1)
+        xs = [x] + [x.clone() for _ in range(sets - 1)]
+        ys = [y] + [torch.empty_like(y) for _ in range(sets - 1)]
+
+        def timed(pairs):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in pairs]
+            for (xi, yi), (a, b) in zip(pairs, evs):
+                a.record(stream)
+                igc.conv_fwd(xi, w, wl.stride, wl.padding, out=yi)
+                b.record(stream)
+            torch.cuda.synchronize()
+            return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+        timed([(x, y)] * 10)
+        warm = timed([(x, y)] * launches)
+        cold = timed([(xs[i % sets], ys[i % sets]) for i in range(launches)])
+        peak = PEAK_TFLOPS[wl.dtype]
+        rec = {"workload": name, "path": kernel_key(wl), "dtype": wl.dtype, "gemm_mnk": [m, n, k],
+               "gflop": round(flops / 1e9, 4), "alg_mb": round(alg_bytes / 1e6, 3), "launches": launches}
+        for tag, t in (("warm", warm), ("cold", cold)):
+            med = float(np.median(t))
+            rec[tag] = {"us_median": round(med, 2), "us_min": round(float(t.min()), 2),
+                        "tflops": round(flops / (med * 1e-6) / 1e12, 2),
+                        "pct_peak": round(100 * flops / (med * 1e-6) / 1e12 / peak, 2),
+                        "alg_gbps": round(alg_bytes / (med * 1e-6) / 1e9, 1)}
+        rec["cold"]["buffer_sets"] = sets
+        print(json.dumps(rec), flush=True)
+        del xs, ys, x, w, y
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +185,10 @@ def main():
                     help="share of one step's output rows the CPU oracle computes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every workload shape on its own (one JSON line each)")
+    ap.add_argument("--launches", type=int, default=50, help="timed launches per shape in --sweep")
+    ap.add_argument("--only", default="", help="comma-separated workload names for --sweep")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -144,6 +201,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.sweep:
+        sweep(args.launches, [n for n in args.only.split(",") if n])
         return
     wls = [WORKLOADS[n] for n in HEADLINE]
     inputs = [make_inputs(wl, dev) for wl in wls]

@@ -103,7 +103,11 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
   static_assert(STAGES >= 2 && STAGES <= 4, "stages");
   static_assert(NL * (STAGES - 2) < 64, "vmcnt");
 
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+  constexpr int OUT_ROWB = BN * 2;      // one output row of the tile in LDS
+  constexpr int OCH = BN / 8;           // its 16-byte pieces
+  constexpr int SMEM = STAGES * STAGE_BYTES > BM * OUT_ROWB ? STAGES * STAGE_BYTES : BM * OUT_ROWB;
+  static_assert(OCH == 8 || OCH == 16, "output row pieces");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -210,29 +214,47 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
     }
   }
 
-  // Epilogue: for output row m = its fragment row, a lane holds runs of 4
+  // Epilogue.  For output row m = its fragment row, a lane holds runs of 4
   // consecutive output channels: channel 16*b' + 4*fg + i (MF = 16) or
   // 32*b' + 8*q + 4*fg + i (MF = 32, q = 0..3) in accumulator element 4*q + i.
+  // The tile goes through LDS (row-major, 16-byte piece k of row r at slot
+  // k ^ (r % OCH)) so that each store writes whole 16-byte pieces of rows.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int a = 0; a < FM; ++a) {
-    const int m = m0 + wm * TM + a * MF + fr;
-    if (m >= p.M) continue;
-    T* yrow = y + (int64_t)m * p.cout;
+    const int row = wm * TM + a * MF + fr;
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        const int n = n0 + wn * TN + b * MF + 8 * q + 4 * fg;
-        if (n + 3 < p.cout) {
-          union { T h[4]; uint2 u; } pk;
+        const int ch = wn * TN + b * MF + 8 * q + 4 * fg;
+        union { T h[4]; uint2 u; } pk;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[a][b][4 * q + i]);
-          *(uint2*)(yrow + n) = pk.u;
+        for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[a][b][4 * q + i]);
+        *(uint2*)(smem + row * OUT_ROWB + (((ch >> 3) ^ (row % OCH)) * 16) + ((ch >> 2) & 1) * 8) = pk.u;
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  constexpr int ORPI = 64 / OCH;        // output rows per wave instruction
+  const bool whole16 = (p.cout & 7) == 0;
+#pragma unroll 4
+  for (int i = 0; i < BM / (4 * ORPI); ++i) {
+    const int row = (4 * i + wave) * ORPI + lane / OCH, k = lane % OCH;
+    const uint4 v = *(const uint4*)(smem + row * OUT_ROWB + ((k ^ (row % OCH)) * 16));
+    const int m = m0 + row;
+    const int n = n0 + k * 8;
+    if (m < p.M) {
+      T* dst = y + (int64_t)m * p.cout + n;
+      if (n + 8 <= p.cout) {
+        if (whole16) {
+          *(uint4*)dst = v;
         } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (n + i < p.cout) yrow[n + i] = from_f32<T>(acc[a][b][4 * q + i]);
+          *(uint2*)dst = make_uint2(v.x, v.y);
+          *(uint2*)(dst + 4) = make_uint2(v.z, v.w);
         }
+      } else if (n + 4 <= p.cout) {
+        *(uint2*)dst = make_uint2(v.x, v.y);
       }
     }
   }

@@ -48,6 +48,7 @@ constexpr int kMaxKW = kSW - kSeg + 1;     // 5
 constexpr int kRowB = 64;                  // bytes per strip position / filter row (32 channels)
 constexpr int kStripBytes = kSegs * kSW * kRowB;   // 36 KB
 constexpr int kA_LOADS = kSegs * kSW / 16 / 4;     // 9 wave-instructions per wave per step
+constexpr int kLdsBytes = 160 * 1024;              // LDS per workgroup on gfx950
 constexpr int kOutRowB = kBN * 2;                  // one output row of the tile in LDS (256 bytes)
 constexpr int kOutTileBytes = kBM * kOutRowB;      // 128 KB
 
@@ -70,11 +71,17 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
   constexpr int B_ROWS = KW * kBN;                 // filter rows per step
   constexpr int B_BYTES = B_ROWS * kRowB;
   constexpr int B_LOADS = B_ROWS * 4 / 256;        // 16-byte pieces per thread
-  constexpr int STAGE = kStripBytes + B_BYTES;
   constexpr int NL = kA_LOADS + B_LOADS;
   static_assert(KW >= 1 && KW <= kMaxKW, "K_w");
   static_assert(NL < 64, "vmcnt");
-  constexpr int SMEM = 2 * STAGE > kOutTileBytes ? 2 * STAGE : kOutTileBytes;
+  // LDS ring: A_ST strip stages, then two filter stages.  Three strip stages
+  // (when they fit) give the strided input loads two steps of lead; the
+  // filter slices, which every workgroup reads and the L2 keeps, get one.
+  constexpr int A_ST = 3 * kStripBytes + 2 * B_BYTES <= kLdsBytes ? 3 : 2;
+  constexpr int B_BASE = A_ST * kStripBytes;
+  constexpr int RING = B_BASE + 2 * B_BYTES;
+  static_assert(RING <= kLdsBytes, "LDS");
+  constexpr int SMEM = RING > kOutTileBytes ? RING : kOutTileBytes;
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
@@ -132,35 +139,57 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
 
   const int nchunks = p.cin / 32;
   const int S = nchunks * p.kd * p.kh;
-  int ic = 0, ikd = 0, ikh = 0;   // (chunk, kd, kh) of the next step to issue
-  int istage = 0;
-  auto issue = [&]() {
-    char* sa = smem + istage * STAGE;
-    char* sb = sa + kStripBytes;
-    // past the last step every load zero-fills (bit masks, not branches)
-    const uint32_t live = ic < nchunks ? ~0u : 0u;
-    const uint32_t xoff = (uint32_t)((ikd * p.xs_d + ikh * p.xs_h + ic * 32) * 2);
+  // step order: kh fastest, then kd, then the channel chunk
+  auto advance = [&](int& ic, int& kd, int& kh) {
+    const int h1 = kh + 1;
+    const bool wh = h1 == p.kh;
+    kh = wh ? 0 : h1;
+    const int d1 = kd + (int)wh;
+    const bool wd = d1 == p.kd;
+    kd = wd ? 0 : d1;
+    ic += (int)wd;
+  };
+  // Past the last step every load zero-fills (bit masks, not branches), so the
+  // issue code runs unconditionally.
+  int a_ic = 0, a_kd = 0, a_kh = 0, a_slot = 0;   // next strip step to issue
+  auto issue_a = [&]() {
+    char* sa = smem + a_slot * kStripBytes;
+    const uint32_t live = a_ic < nchunks ? ~0u : 0u;
+    const uint32_t xoff = (uint32_t)((a_kd * p.xs_d + a_kh * p.xs_h + a_ic * 32) * 2);
 #pragma unroll
     for (int q = 0; q < kA_LOADS; ++q) {
-      const bool ok = (((a_mask[q] & live) >> ikd) & (a_mask[q] >> (16 + ikh)) & 1u) != 0u;
+      const bool ok = (((a_mask[q] & live) >> a_kd) & (a_mask[q] >> (16 + a_kh)) & 1u) != 0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xr, (lds_ptr_t)(sa + ((4 * q + wave) * 16) * kRowB), 16, ok ? a_base[q] + xoff : kOutOfRange,
           0, 0, 0);
     }
-    const uint32_t woff = (uint32_t)(((ikd * p.kh + ikh) * p.kw * p.cin + ic * 32) * 2);
+    advance(a_ic, a_kd, a_kh);
+    a_slot = a_slot + 1 == A_ST ? 0 : a_slot + 1;
+  };
+  int b_ic = 0, b_kd = 0, b_kh = 0, b_slot = 0;   // next filter step to issue
+  auto issue_b = [&]() {
+    char* sb = smem + B_BASE + b_slot * B_BYTES;
+    const uint32_t live = b_ic < nchunks ? ~0u : 0u;
+    const uint32_t woff = (uint32_t)(((b_kd * p.kh + b_kh) * p.kw * p.cin + b_ic * 32) * 2);
 #pragma unroll
     for (int s = 0; s < B_LOADS; ++s)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wr, (lds_ptr_t)(sb + (s * 256 + wave * 64) * 16), 16, (b_base[s] + woff) | (~live & kOutOfRange), 0,
           0, 0);
-    const int h1 = ikh + 1;
-    const bool wh = h1 == p.kh;
-    ikh = wh ? 0 : h1;
-    const int d1 = ikd + (int)wh;
-    const bool wd = d1 == p.kd;
-    ikd = wd ? 0 : d1;
-    ic += (int)wd;
-    istage ^= 1;
+    advance(b_ic, b_kd, b_kh);
+    b_slot ^= 1;
+  };
+  // loads a wave may still have in flight when it needs the next step: the
+  // strip loads issued after that step's filter loads
+  constexpr int WAIT_N = A_ST == 3 ? kA_LOADS : 0;
+  auto issue_ahead = [&]() {
+    if constexpr (A_ST == 3) {
+      issue_b();                           // filter: two steps ahead
+      issue_a();                           // strip: three steps ahead
+    } else {
+      issue_a();
+      issue_b();
+    }
   };
 
   // ---- fragment addresses: lane (r = lane % 32, g2 = lane / 32) ----
@@ -174,7 +203,7 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
       a_addr[kw][ks] = (wave * 4 * kSW + o) * kRowB + swz(o, 2 * ks + g2) * 16;
     }
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) b_addr[ks] = kStripBytes + r * kRowB + swz(r, 2 * ks + g2) * 16;
+  for (int ks = 0; ks < 2; ++ks) b_addr[ks] = r * kRowB + swz(r, 2 * ks + g2) * 16;
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -192,11 +221,11 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
   // arithmetic of those loads is interleaved with the MFMAs.
   constexpr int NBLK = 2 * KW;
   V8 fa[2][4], fb[2][4];
-  auto read_block = [&](V8(&af)[4], V8(&bf)[4], const char* st, int kw, int ks) {
+  auto read_block = [&](V8(&af)[4], V8(&bf)[4], const char* sa, const char* sb, int kw, int ks) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) af[a] = *(const V8*)(st + a_addr[kw][ks] + a * kSW * kRowB);
+    for (int a = 0; a < 4; ++a) af[a] = *(const V8*)(sa + a_addr[kw][ks] + a * kSW * kRowB);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) bf[b] = *(const V8*)(st + b_addr[ks] + (kw * kBN + b * 32) * kRowB);
+    for (int b = 0; b < 4; ++b) bf[b] = *(const V8*)(sb + b_addr[ks] + (kw * kBN + b * 32) * kRowB);
   };
   auto mma_block = [&](const V8(&af)[4], const V8(&bf)[4]) {
 #pragma unroll
@@ -204,14 +233,14 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[a][b] = mfma32x32x16(bf[b], af[a], acc[a][b]);
   };
-  // one step on stage st; unless it is the last, also hand over to stage sn
-  auto run_step = [&](const char* st, const char* sn, auto last) {
+  // one step on stages (sa, sb); unless it is the last, also hand over to (na, nb)
+  auto run_step = [&](const char* sa, const char* sb, const char* na, const char* nb, auto last) {
     constexpr bool kLast = decltype(last)::value;
 #pragma unroll
     for (int j = 0; j < NBLK; ++j) {
       const int cur = j & 1, nxt = cur ^ 1;
       if (j + 1 < NBLK) {
-        read_block(fa[nxt], fb[nxt], st, (j + 1) >> 1, (j + 1) & 1);
+        read_block(fa[nxt], fb[nxt], sa, sb, (j + 1) >> 1, (j + 1) & 1);
         mma_block(fa[cur], fb[cur]);
         // one fragment read in the shadow of each of the first 8 MFMAs
 #pragma unroll
@@ -222,11 +251,11 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         __builtin_amdgcn_sched_barrier(0);
       } else if constexpr (!kLast) {
-        // every wave's reads of stage st have returned; the next step has landed
+        // every wave's reads of this step have returned; the next step has landed
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        wait_vmcnt_barrier<0>();
-        read_block(fa[nxt], fb[nxt], sn, 0, 0);
-        issue();                            // two steps ahead, into stage st
+        wait_vmcnt_barrier<WAIT_N>();
+        read_block(fa[nxt], fb[nxt], na, nb, 0, 0);
+        issue_ahead();                      // into the slots this step freed
         mma_block(fa[cur], fb[cur]);
         // in the shadow of each MFMA: a fragment read (first 8), load address VALU, a load
 #pragma unroll
@@ -244,14 +273,32 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
   };
 
   if (S > 0) {
-    issue();                                // step 0 -> stage 0
-    wait_vmcnt_barrier<0>();
-    issue();                                // step 1 -> stage 1
-    read_block(fa[0], fb[0], smem, 0, 0);
-    for (int s = 0; s + 1 < S; ++s)
-      run_step(smem + (s & 1) * STAGE, smem + ((s + 1) & 1) * STAGE, std::false_type{});
-    run_step(smem + ((S - 1) & 1) * STAGE, nullptr, std::true_type{});
+    if constexpr (A_ST == 3) {
+      issue_a();                            // strip 0
+      issue_b();                            // filter 0
+      issue_a();                            // strip 1
+      wait_vmcnt_barrier<kA_LOADS>();       // step 0 landed
+      issue_b();                            // filter 1
+      issue_a();                            // strip 2
+    } else {
+      issue_a();
+      issue_b();
+      wait_vmcnt_barrier<0>();              // step 0 landed
+      issue_a();
+      issue_b();
+    }
+    read_block(fa[0], fb[0], smem, smem + B_BASE, 0, 0);
+    int ra = 0, rb = 0;                     // slots of the step being computed
+    for (int s = 0; s + 1 < S; ++s) {
+      const int ra1 = ra + 1 == A_ST ? 0 : ra + 1, rb1 = rb ^ 1;
+      run_step(smem + ra * kStripBytes, smem + B_BASE + rb * B_BYTES, smem + ra1 * kStripBytes,
+               smem + B_BASE + rb1 * B_BYTES, std::false_type{});
+      ra = ra1;
+      rb = rb1;
+    }
+    run_step(smem + ra * kStripBytes, smem + B_BASE + rb * B_BYTES, nullptr, nullptr, std::true_type{});
   }
+
   // ---- epilogue: the tile goes through LDS so that each store writes whole
   // 16-byte pieces of output rows (4 rows of 128 channels per wave
   // instruction) instead of 8 bytes in each of 32 rows.  Lane (r, g2) holds
