@@ -277,7 +277,10 @@ hipError_t launch_cfg(const ConvParams& p, const void* x, const void* w, void* y
 // of them for every problem, for tile-size sweeps; by default the choice below
 // depends on the problem size and channel alignment.
 constexpr int variant_bk(int v) {
-  return (v == 1 || v == 4 || v == 7 || v == 41 || v == 43 || v == 45 || v == 47) ? 64 : 32;
+  return (v == 1 || v == 4 || v == 7 || v == 9 || v == 10 || v == 12 || v == 13 || v == 41 || v == 43 ||
+          v == 45 || v == 47)
+             ? 64
+             : 32;
 }
 
 template <typename T>
@@ -290,6 +293,11 @@ hipError_t launch_variant(int v, const ConvParams& p, const void* x, const void*
     case 4: return launch_cfg<T, 128, 128, 64, 2, 2, 2, 2, 16>(p, x, w, y, s);
     case 7: return launch_cfg<T, 64, 128, 64, 1, 4, 3, 2, 16>(p, x, w, y, s);
     case 8: return launch_cfg<T, 128, 64, 32, 2, 2, 3, 2, 16>(p, x, w, y, s);
+    case 9: return launch_cfg<T, 64, 64, 64, 2, 2, 4, 2, 16>(p, x, w, y, s);
+    case 10: return launch_cfg<T, 64, 128, 64, 1, 4, 4, 1, 16>(p, x, w, y, s);
+    case 11: return launch_cfg<T, 64, 64, 32, 2, 2, 4, 3, 16>(p, x, w, y, s);
+    case 12: return launch_cfg<T, 32, 128, 64, 1, 4, 4, 2, 16>(p, x, w, y, s);
+    case 13: return launch_cfg<T, 64, 64, 64, 2, 2, 3, 3, 16>(p, x, w, y, s);
     // 32x32x16 MFMA blocks
     case 41: return launch_cfg<T, 256, 128, 64, 4, 1, 2, 1, 32>(p, x, w, y, s);
     case 42: return launch_cfg<T, 256, 128, 32, 4, 1, 2, 2, 32>(p, x, w, y, s);
@@ -313,7 +321,7 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
   const bool bk64 = p.cin % 64 == 0;
   const long tiles_256 = (long)((p.M + 255) / 256) * ((p.cout + 127) / 128);
   if (tiles_256 >= 256) return launch_variant<T>(bk64 ? 4 : 3, p, x, w, y, s);
-  return launch_variant<T>(bk64 ? 7 : 8, p, x, w, y, s);
+  return launch_variant<T>(bk64 ? 9 : 8, p, x, w, y, s);
 }
 
 }  // namespace

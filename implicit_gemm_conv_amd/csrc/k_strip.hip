@@ -26,6 +26,17 @@
 // per-lane constant (one per tap and k-half) plus an immediate.
 // Loads are 16-byte buffer loads straight into LDS; a position in the padding
 // gets an offset past the buffer end, which the range check turns into zeros.
+//
+// Pipeline (K_w <= 3, where three strip stages and two filter stages fit in
+// LDS): the strip of step s+2 is issued in pieces from the MFMA blocks of step
+// s and the filter slices of step s+2 right after the barrier that ends step
+// s; both must land by the barrier that ends step s+1.  Spreading the strip
+// loads over the step keeps their direct-to-LDS writes from arriving in one
+// burst (they slow the fragment reads they overlap).  With K_w = 4, 5 there are
+// two stages of each and all loads of step s+2 go out after that barrier.
+// Fragments are double-buffered in registers, so a block's LDS reads run under
+// the previous block's MFMAs.  The epilogue stages the tile through LDS so
+// stores write whole 16-byte pieces of rows.
 #include <type_traits>
 
 #include "conv_device.h"
@@ -152,20 +163,23 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
   // Past the last step every load zero-fills (bit masks, not branches), so the
   // issue code runs unconditionally.
   int a_ic = 0, a_kd = 0, a_kh = 0, a_slot = 0;   // next strip step to issue
-  auto issue_a = [&]() {
+  auto issue_a_part = [&](int q0, int q1) {
     char* sa = smem + a_slot * kStripBytes;
     const uint32_t live = a_ic < nchunks ? ~0u : 0u;
     const uint32_t xoff = (uint32_t)((a_kd * p.xs_d + a_kh * p.xs_h + a_ic * 32) * 2);
 #pragma unroll
-    for (int q = 0; q < kA_LOADS; ++q) {
+    for (int q = q0; q < q1; ++q) {
       const bool ok = (((a_mask[q] & live) >> a_kd) & (a_mask[q] >> (16 + a_kh)) & 1u) != 0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xr, (lds_ptr_t)(sa + ((4 * q + wave) * 16) * kRowB), 16, ok ? a_base[q] + xoff : kOutOfRange,
           0, 0, 0);
     }
-    advance(a_ic, a_kd, a_kh);
-    a_slot = a_slot + 1 == A_ST ? 0 : a_slot + 1;
+    if (q1 == kA_LOADS) {
+      advance(a_ic, a_kd, a_kh);
+      a_slot = a_slot + 1 == A_ST ? 0 : a_slot + 1;
+    }
   };
+  auto issue_a = [&]() { issue_a_part(0, kA_LOADS); };
   int b_ic = 0, b_kd = 0, b_kh = 0, b_slot = 0;   // next filter step to issue
   auto issue_b = [&]() {
     char* sb = smem + B_BASE + b_slot * B_BYTES;
@@ -182,10 +196,12 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
   // loads a wave may still have in flight when it needs the next step: the
   // strip loads issued after that step's filter loads
   constexpr int WAIT_N = A_ST == 3 ? kA_LOADS : 0;
+  // Loads issued at the step barrier: with three strip stages only the filter
+  // slices (the strip loads are spread over the next step's blocks, which keeps
+  // the direct-to-LDS writes from piling onto the fragment reads at one point).
   auto issue_ahead = [&]() {
     if constexpr (A_ST == 3) {
       issue_b();                           // filter: two steps ahead
-      issue_a();                           // strip: three steps ahead
     } else {
       issue_a();
       issue_b();
@@ -241,14 +257,19 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
       const int cur = j & 1, nxt = cur ^ 1;
       if (j + 1 < NBLK) {
         read_block(fa[nxt], fb[nxt], sa, sb, (j + 1) >> 1, (j + 1) & 1);
+        // part of the strip two steps ahead (its slot was freed at the last barrier)
+        constexpr int NB1 = NBLK - 1;
+        const int q0 = (j * kA_LOADS) / NB1, q1 = ((j + 1) * kA_LOADS) / NB1;
+        if constexpr (A_ST == 3) issue_a_part(q0, q1);
         mma_block(fa[cur], fb[cur]);
-        // one fragment read in the shadow of each of the first 8 MFMAs
+        // in the shadow of each MFMA: a fragment read (first 8), load address VALU, a load
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 16; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         __builtin_amdgcn_sched_barrier(0);
       } else if constexpr (!kLast) {
         // every wave's reads of this step have returned; the next step has landed
@@ -278,8 +299,7 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
       issue_b();                            // filter 0
       issue_a();                            // strip 1
       wait_vmcnt_barrier<kA_LOADS>();       // step 0 landed
-      issue_b();                            // filter 1
-      issue_a();                            // strip 2
+      issue_b();                            // filter 1; strip 2 goes out during step 0
     } else {
       issue_a();
       issue_b();
