@@ -39,6 +39,8 @@ hipError_t launch_brick(const ConvParams& p, int dtype, const void* x, const voi
                         hipStream_t s);
 hipError_t launch_strip(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
                         hipStream_t s);
+hipError_t launch_runs(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                       hipStream_t s);
 
 // Whether a path accepts a problem (host-side rules mirrored in convfwd.h).
 bool main_accepts(const ConvParams& p, int dtype);
@@ -46,5 +48,6 @@ bool flatk_accepts(const ConvParams& p, int dtype);
 bool rows_accepts(const ConvParams& p, int dtype);
 bool brick_accepts(const ConvParams& p, int dtype);
 bool strip_accepts(const ConvParams& p, int dtype);
+bool runs_accepts(const ConvParams& p, int dtype);
 
 }  // namespace convfwd

@@ -87,7 +87,7 @@ int auto_path(const ConvParams& p, int dtype) {
   if (p.kw >= 2 && convfwd::strip_accepts(p, dtype)) return CONVFWD_PATH_STRIP;
   if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;
-  if (convfwd::flatk_accepts(p, dtype)) return CONVFWD_PATH_FLATK;
+  if (convfwd::runs_accepts(p, dtype)) return CONVFWD_PATH_RUNS;
   return CONVFWD_PATH_DIRECT;
 }
 
@@ -99,6 +99,7 @@ bool path_accepts(int path, const ConvParams& p, int dtype) {
     case CONVFWD_PATH_DIRECT: return true;
     case CONVFWD_PATH_BRICK: return convfwd::brick_accepts(p, dtype);
     case CONVFWD_PATH_STRIP: return convfwd::strip_accepts(p, dtype);
+    case CONVFWD_PATH_RUNS: return convfwd::runs_accepts(p, dtype);
     default: return false;
   }
 }
@@ -121,6 +122,7 @@ int run(const convfwd_desc* desc, int path, const void* x, const void* w, void* 
     case CONVFWD_PATH_ROWS: e = convfwd::launch_rows(p, desc->dtype, x, w, y, s); break;
     case CONVFWD_PATH_BRICK: e = convfwd::launch_brick(p, desc->dtype, x, w, y, s); break;
     case CONVFWD_PATH_STRIP: e = convfwd::launch_strip(p, desc->dtype, x, w, y, s); break;
+    case CONVFWD_PATH_RUNS: e = convfwd::launch_runs(p, desc->dtype, x, w, y, s); break;
     default: e = convfwd::launch_direct(p, desc->dtype, x, w, y, s); break;
   }
   if (e != hipSuccess) return CONVFWD_ERR_LAUNCH;
@@ -155,7 +157,7 @@ int conv_fwd(const convfwd_desc* desc, const void* x, const void* w, void* y, vo
 
 int conv_fwd_path(const convfwd_desc* desc, int path, const void* x, const void* w, void* y,
                   void* stream) {
-  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_STRIP) return CONVFWD_ERR_UNSUPPORTED;
+  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_RUNS) return CONVFWD_ERR_UNSUPPORTED;
   return run(desc, path, x, w, y, stream);
 }
 
@@ -181,6 +183,7 @@ const char* conv_path_name(int path) {
     case CONVFWD_PATH_DIRECT: return "direct";
     case CONVFWD_PATH_BRICK: return "brick";
     case CONVFWD_PATH_STRIP: return "strip";
+    case CONVFWD_PATH_RUNS: return "runs";
     default: return "unknown";
   }
 }

@@ -1,0 +1,314 @@
+// k_runs.hip -- implicit GEMM for any C_in (the unaligned-channel tail path)
+// and fp32, reading the im2col matrix as contiguous runs.
+//
+// With K ordered (kd, kh, kw, c), the K_w * C_in columns of one (kd, kh) form
+// a run that is contiguous in memory on both sides of the product: in x the
+// K_w window positions of an output are adjacent along w with all their
+// channels ("Convolutions" tutorial, section 5: the im2col row of an output
+// is its window, flattened), and in the filter (C_out, K_d, K_h, K_w, C_in)
+// the same run is one slice of a filter row.  The GEMM depth is walked run by
+// run, each run cut into steps of 32 columns (the last one zero-padded), so a
+// step of an output row is 32 consecutive input elements.  Rows of odd
+// channel counts are only 2-byte aligned: a step is fetched as 16-byte pieces
+// with unaligned buffer loads, and the columns of window positions that fall
+// in the padding (or past the run) are zeroed with branch-free masks.  Pieces
+// that would start before x or reach past the end of a tensor (only possible
+// on its first and last lines) are fetched element by element, since the
+// buffer range check drops any dword that is not wholly inside the tensor.
+//
+// Pipeline: the pieces of DEPTH steps are in flight in registers at once; each
+// step's pieces are masked and written to a double-buffered LDS tile (rows
+// padded by 16 bytes so that fragment reads of 16 rows hit distinct banks),
+// then read as MFMA fragments: v_mfma_f32_16x16x32_{f16,bf16}, or for fp32
+// eight v_mfma_f32_16x16x4_f32 per step.  Four waves split the tile along M.
+#include "conv_device.h"
+
+namespace convfwd {
+
+namespace {
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr int kBK = 32;     // GEMM columns per step
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct RunFrag;
+template <> struct RunFrag<_Float16> { typedef half8_t type; };
+template <> struct RunFrag<__bf16> { typedef bf168_t type; };
+template <> struct RunFrag<float> { struct type { f32x4_t lo, hi; }; };
+
+__device__ __forceinline__ f32x4_t run_mfma(half8_t a, half8_t b, f32x4_t c) { return mfma16x16x32(a, b, c); }
+__device__ __forceinline__ f32x4_t run_mfma(bf168_t a, bf168_t b, f32x4_t c) { return mfma16x16x32(a, b, c); }
+// Lane group g supplies column 8g + e to the e-th 16x16x4 product; over e < 8
+// and g < 4 that covers the 32 columns of the step once each.
+template <typename F>
+__device__ __forceinline__ f32x4_t run_mfma(const F& a, const F& b, f32x4_t c) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], c, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
+  return c;
+}
+
+// Keep the elements j of a 16-byte piece with jl <= j < jh, zero the others.
+template <int EB>
+__device__ __forceinline__ u4 keep_range(u4 v, int jl, int jh) {
+  u4 r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    if constexpr (EB == 4) {
+      r[d] = (d >= jl && d < jh) ? v[d] : 0u;
+    } else {
+      const uint32_t lo = (2 * d >= jl && 2 * d < jh) ? 0x0000ffffu : 0u;
+      const uint32_t hi = (2 * d + 1 >= jl && 2 * d + 1 < jh) ? 0xffff0000u : 0u;
+      r[d] = v[d] & (lo | hi);
+    }
+  }
+  return r;
+}
+
+// The 16 bytes at element offset e of a tensor of `bytes` bytes, where only
+// elements j with jl <= j < jh are wanted: one unaligned 16-byte load when the
+// piece lies wholly inside the tensor, else element loads of the wanted ones.
+template <int EB>
+__device__ __forceinline__ u4 load_piece(__amdgpu_buffer_rsrc_t rsrc, int e, bool ok, int jl, int jh,
+                                         int bytes) {
+  const int bo = e * EB;
+  const bool whole = ok && bo >= 0 && bo <= bytes - 16;
+  u4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, whole ? (uint32_t)bo : kOutOfRange, 0, 0);
+  if (ok && !whole) {   // first or last line of the tensor: rare, element by element
+    constexpr int EPC = 16 / EB;
+#pragma unroll
+    for (int j = 0; j < EPC; ++j) {
+      const int be = bo + j * EB;
+      const bool want = j >= jl && j < jh && be >= 0 && be <= bytes - EB;
+      if constexpr (EB == 4) {
+        v[j] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, want ? (uint32_t)be : kOutOfRange, 0, 0);
+      } else {
+        const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rsrc, want ? (uint32_t)be : kOutOfRange, 0, 0);
+        v[j >> 1] = (j & 1) ? ((v[j >> 1] & 0x0000ffffu) | (h << 16)) : ((v[j >> 1] & 0xffff0000u) | h);
+      }
+    }
+  }
+  return v;
+}
+
+template <typename T, int BM, int BN, int DEPTH>
+__global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T* __restrict__ x,
+                                                           const T* __restrict__ w, T* __restrict__ y,
+                                                           int tiles_n, int x_bytes, int w_bytes) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef typename RunFrag<T>::type F;
+  constexpr int EB = sizeof(T);
+  constexpr int EPC = 16 / EB;                 // elements per 16-byte piece
+  constexpr int CPR = kBK / EPC;               // pieces per row per step
+  constexpr int ROWB = kBK * EB + 16;          // padded LDS row
+  constexpr int A_PER = BM * CPR / 256;        // A pieces per thread per step
+  constexpr int B_PIECES = BN * CPR;
+  constexpr int B_PER = (B_PIECES + 255) / 256;
+  constexpr int TM = BM / 4;                   // rows per wave
+  constexpr int FM = TM / 16, FN = BN / 16;
+  constexpr int STAGE = (BM + BN) * ROWB;
+  static_assert(BM * CPR % 256 == 0 && TM % 16 == 0 && BN % 16 == 0, "tile");
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (tile / tiles_n) * BM;
+  const int n0 = (tile % tiles_n) * BN;
+  const __amdgpu_buffer_rsrc_t xr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, x_bytes, kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t wr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, w_bytes, kRawBufferFlags);
+
+  const int run = p.kw * p.cin;                // columns of one (kd, kh)
+  const int sps = (run + kBK - 1) / kBK;       // steps per run
+  const int S = p.kd * p.kh * sps;
+
+  // A pieces: thread piece i -> tile row, piece q; the run of that output row
+  // at (kd, kh) = (0, 0) starts at element a_e[i] - q * EPC, and its columns
+  // [a_lo, a_hi) (relative to this piece's first column at step column 0) lie
+  // inside the input along w.
+  int a_e[A_PER], a_lo[A_PER], a_hi[A_PER];
+  uint32_t a_dh[A_PER];   // depth-tap bits | height-tap bits << 16
+  int a_ldsoff[A_PER];
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i) {
+    const int c = tid + 256 * i, row = c / CPR, q = c % CPR;
+    const RowInfo ri = decode_row(p, m0 + row);
+    const int lo_w = ri.mw ? __builtin_ctz(ri.mw) : 0;
+    const int hi_w = ri.mw ? 32 - __builtin_clz(ri.mw) : 0;
+    a_e[i] = ri.base + q * EPC;
+    a_lo[i] = lo_w * p.cin - q * EPC;
+    a_hi[i] = hi_w * p.cin - q * EPC;
+    a_dh[i] = ri.md | (ri.mh << 16);
+    a_ldsoff[i] = row * ROWB + q * 16;
+  }
+  // B pieces: filter row n0 + brow, piece bq; columns past the run are zero.
+  int b_e[B_PER], b_hi[B_PER], b_ldsoff[B_PER];
+  bool b_ok[B_PER];
+#pragma unroll
+  for (int j = 0; j < B_PER; ++j) {
+    const int c = tid + 256 * j, brow = c / CPR, bq = c % CPR;
+    const int co = n0 + brow;
+    b_ok[j] = c < B_PIECES && co < p.cout;
+    b_e[j] = co * p.K + bq * EPC;
+    b_hi[j] = run - bq * EPC;
+    b_ldsoff[j] = BM * ROWB + brow * ROWB + bq * 16;
+  }
+
+  // Loads of the step (kd, kh, k0) into register slot `slot`; steps past the
+  // end load nothing.
+  u4 ra[DEPTH][A_PER], rb[DEPTH][B_PER];
+  int l_kd = 0, l_kh = 0, l_k0 = 0, l_step = 0;
+  int s_k0[DEPTH];   // column offset of the step in each slot (for the masks)
+  auto load_step = [&](int slot) {
+    const bool live = l_step < S;
+    const int xo = l_kd * p.xs_d + l_kh * p.xs_h + l_k0;
+    const int wo = (l_kd * p.kh + l_kh) * run + l_k0;
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      const bool ok = live && ((a_dh[i] >> l_kd) & (a_dh[i] >> (16 + l_kh)) & 1u);
+      ra[slot][i] = load_piece<EB>(xr, a_e[i] + xo, ok, a_lo[i] - l_k0, a_hi[i] - l_k0, x_bytes);
+    }
+#pragma unroll
+    for (int j = 0; j < B_PER; ++j)
+      rb[slot][j] = load_piece<EB>(wr, b_e[j] + wo, live && b_ok[j], 0, b_hi[j] - l_k0, w_bytes);
+    s_k0[slot] = l_k0;
+    l_k0 += kBK;
+    if (l_k0 >= run) {
+      l_k0 = 0;
+      if (++l_kh == p.kh) {
+        l_kh = 0;
+        ++l_kd;
+      }
+    }
+    ++l_step;
+  };
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int b = 0; b < FN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, fg = lane >> 4;
+
+#pragma unroll
+  for (int t = 0; t < DEPTH; ++t) load_step(t);
+
+  // One step on register slot `slot`: mask its pieces into LDS stage
+  // (step & 1), then the MFMAs; the slot is refilled with the step DEPTH on.
+  auto run_step = [&](int step, int slot) {
+    char* st = smem + (step & 1) * STAGE;
+    const int k0 = s_k0[slot];
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i)
+      *(u4*)(st + a_ldsoff[i]) = keep_range<EB>(ra[slot][i], a_lo[i] - k0, a_hi[i] - k0);
+#pragma unroll
+    for (int j = 0; j < B_PER; ++j)
+      if (tid + 256 * j < B_PIECES) *(u4*)(st + b_ldsoff[j]) = keep_range<EB>(rb[slot][j], 0, b_hi[j] - k0);
+    // The step's pieces are visible to every wave; the LDS stage written two
+    // steps from now is no longer being read.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    load_step(slot);
+    if (step < S) {
+      F af[FM], bf[FN];
+#pragma unroll
+      for (int a = 0; a < FM; ++a) af[a] = *(const F*)(st + (wave * TM + a * 16 + fr) * ROWB + fg * 8 * EB);
+#pragma unroll
+      for (int b = 0; b < FN; ++b) bf[b] = *(const F*)(st + BM * ROWB + (b * 16 + fr) * ROWB + fg * 8 * EB);
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) acc[a][b] = run_mfma(bf[b], af[a], acc[a][b]);
+    }
+  };
+  for (int s = 0; s < S; s += DEPTH) {
+#pragma unroll
+    for (int t = 0; t < DEPTH; ++t) run_step(s + t, t);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // loads past the end
+
+  // Epilogue: lane holds D[n = 4*fg + i][m = fr] of each 16x16 block.
+  const bool vec_ok = (p.cout & 3) == 0;
+#pragma unroll
+  for (int a = 0; a < FM; ++a) {
+    const int m = m0 + wave * TM + a * 16 + fr;
+    if (m >= p.M) continue;
+    T* yrow = y + (int64_t)m * p.cout;
+#pragma unroll
+    for (int b = 0; b < FN; ++b) {
+      const int n = n0 + b * 16 + fg * 4;
+      if (vec_ok && n + 3 < p.cout) {
+        if constexpr (EB == 2) {
+          union { T h[4]; uint2 u; } pk;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[a][b][i]);
+          *(uint2*)(yrow + n) = pk.u;
+        } else {
+          *(f32x4_t*)(yrow + n) = acc[a][b];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n + i < p.cout) yrow[n + i] = from_f32<T>(acc[a][b][i]);
+      }
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// Steps in flight in registers: 8 with 64-row tiles (the small problems they
+// serve have few workgroups), else 2 (on (4,32^3,65) two steps ahead with four
+// resident workgroups per CU beat four or six steps ahead with fewer: 115 us
+// against 149 and 158).
+template <typename T, int BM, int BN>
+hipError_t launch_cfg(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
+  constexpr int DEPTH = BM == 64 && (sizeof(T) == 2 || BN < 128) ? 8 : 2;
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int tiles_n = (p.cout + BN - 1) / BN;
+  const int xb = (int)((int64_t)p.n * p.xs_n * sizeof(T));
+  const int wb = (int)((int64_t)p.cout * p.K * sizeof(T));
+  hipLaunchKernelGGL((conv_runs_kernel<T, BM, BN, DEPTH>), dim3(tiles_m * tiles_n), dim3(256), 0, s, p,
+                     (const T*)x, (const T*)w, (T*)y, tiles_n, xb, wb);
+  return hipGetLastError();
+}
+
+// Column tile: the smallest of 32, 48, 64, 80, 128 that holds C_out (128 and
+// several column tiles beyond that); row tile 128 when that still gives a few
+// hundred tiles, else 64 (fp32 always 64).
+template <typename T, int BM>
+hipError_t launch_bn(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
+  if (p.cout <= 32) return launch_cfg<T, BM, 32>(p, x, w, y, s);
+  if (p.cout <= 48) return launch_cfg<T, BM, 48>(p, x, w, y, s);
+  if (p.cout <= 64) return launch_cfg<T, BM, 64>(p, x, w, y, s);
+  if (p.cout <= 80) return launch_cfg<T, BM, 80>(p, x, w, y, s);
+  return launch_cfg<T, BM, 128>(p, x, w, y, s);
+}
+
+template <typename T>
+hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if ((p.M + 127) / 128 >= 512) return launch_bn<T, 128>(p, x, w, y, s);
+  }
+  return launch_bn<T, 64>(p, x, w, y, s);
+}
+
+}  // namespace
+
+bool runs_accepts(const ConvParams& p, int dtype) {
+  (void)dtype;
+  return p.kd <= 16 && p.kh <= 16 && p.kw <= 16;
+}
+
+hipError_t launch_runs(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                       hipStream_t s) {
+  if (dtype == kF32) return launch_typed<float>(p, x, w, y, s);
+  if (dtype == kF16) return launch_typed<_Float16>(p, x, w, y, s);
+  return launch_typed<__bf16>(p, x, w, y, s);
+}
+
+}  // namespace convfwd

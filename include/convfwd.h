@@ -79,10 +79,13 @@ typedef enum {
                               per dim and a brick that fits: the input brick of a box of up to
                               512 outputs staged in LDS per 16-channel chunk, every tap read
                               from it, MFMA */
-  CONVFWD_PATH_STRIP = 6   /* fp16/bf16, C_in % 32 == 0, C_out % 4 == 0, stride 1 along w,
+  CONVFWD_PATH_STRIP = 6,  /* fp16/bf16, C_in % 32 == 0, C_out % 4 == 0, stride 1 along w,
                               W_out % 32 == 0, K_w <= 5, K_d, K_h <= 16: per (channel chunk,
                               kd, kh) one input strip per 32-output w-segment staged in LDS,
                               all K_w taps read from it, 512 x 128 tiles, MFMA */
+  CONVFWD_PATH_RUNS = 7    /* any dtype and C_in, filter <= 16 per dim (the unaligned-channel
+                              tail path and fp32): the K_w * C_in columns of each (kd, kh) read
+                              as one contiguous run, 16-byte unaligned pieces, MFMA */
 } convfwd_path;
 
 /* Problem descriptor.  All extents in elements. */
@@ -119,7 +122,7 @@ int conv_fwd_path(const convfwd_desc* desc, int path, const void* x, const void*
 /* Static message for a return code; never NULL. */
 const char* conv_strerror(int code);
 
-/* Static name of a path ("auto", "main", "flatk", "rows", "direct", "brick", "strip");
+/* Static name of a path ("auto", "main", "flatk", "rows", "direct", "brick", "strip", "runs");
  * never NULL. */
 const char* conv_path_name(int path);
 

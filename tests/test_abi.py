@@ -125,6 +125,7 @@ def test_forced_path_rules():
     # filters wider than 16 only on the direct path
     d = _desc(n=0, w=40, k_w=17)
     assert lib.conv_fwd_path(ctypes.byref(d), 2, None, None, None, None) == -3
+    assert lib.conv_fwd_path(ctypes.byref(d), 7, None, None, None, None) == -3
     assert lib.conv_fwd_path(ctypes.byref(d), 4, None, None, None, None) == 0
 
 
@@ -132,18 +133,18 @@ def test_strerror_and_path_names():
     lib = igc.lib()
     for code in range(-7, 1):
         assert lib.conv_strerror(code)
-    assert [lib.conv_path_name(i).decode() for i in range(7)] == ["auto", "main", "flatk", "rows",
-                                                                  "direct", "brick", "strip"]
+    assert [lib.conv_path_name(i).decode() for i in range(8)] == ["auto", "main", "flatk", "rows",
+                                                                  "direct", "brick", "strip", "runs"]
 
 
 EXPECTED_PATHS = {
-    "c1_conv3d_fp32_n1_8c16_o32": "flatk",
+    "c1_conv3d_fp32_n1_8c16_o32": "runs",
     "c2_conv2d_fp16_n32_56c256_o256": "main",
     "c4a_conv3d_fp16_n4_32c128_o128": "strip",
     "c4b_conv3d_fp16_n1_64c64_o128": "strip",
     "c4c_conv3d_fp16_n4_32c64_o128_s2": "main",
-    "c5a_conv3d_bf16_n4_32c65_o65": "flatk",
-    "c5b_conv3d_bf16_n4_16c21_o21": "flatk",
+    "c5a_conv3d_bf16_n4_32c65_o65": "runs",
+    "c5b_conv3d_bf16_n4_16c21_o21": "runs",
     "c5c_conv3d_bf16_n4_32c64_o128_k311": "main",
     "c5d_conv3d_bf16_n4_32c64_o128_k133": "strip",
     "c3_conv2d_fp16_stem_n64_224c3_o64_k7s2": "rows",

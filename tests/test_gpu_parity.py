@@ -55,7 +55,7 @@ CASES = [
     _case("strip_fp16_2d_k5_o132", "fp16", (3, 9, 32, 32), (132, 5, 5, 32), (1, 1), (1, 2), seed=23),
     _case("strip_fp16_hs2_w32", "fp16", (2, 7, 9, 34, 64), (64, 3, 3, 3, 64), (2, 2, 1), (1, 0, 0), seed=24),
 ]
-PATHS = ["strip", "main", "brick", "rows", "flatk", "direct"]
+PATHS = ["strip", "main", "brick", "rows", "runs", "flatk", "direct"]
 
 
 def _accepts(wl, path):
@@ -140,6 +140,11 @@ EXACT = [
     ("flatk", "bf16", (2, 5, 6, 7, 5), (3, 3, 3), (1, 2, 1), (1, 1, 2)),
     ("flatk", "fp32", (1, 4, 9, 8, 3), (1, 7, 7), (1, 2, 2), (0, 3, 3)),
     ("flatk", "fp16", (2, 5, 6, 7, 65), (3, 3, 3), (3, 1, 2), (3, 1, 0)),
+    ("runs", "bf16", (2, 5, 6, 7, 5), (3, 3, 3), (1, 2, 1), (1, 1, 2)),
+    ("runs", "fp32", (1, 4, 9, 8, 3), (1, 7, 7), (1, 2, 2), (0, 3, 3)),
+    ("runs", "fp16", (2, 5, 6, 7, 65), (3, 3, 3), (3, 1, 2), (3, 1, 0)),
+    ("runs", "bf16", (1, 4, 5, 40, 21), (3, 3, 5), (1, 1, 1), (1, 1, 2)),
+    ("runs", "fp32", (2, 3, 4, 5, 33), (2, 3, 3), (1, 1, 1), (1, 1, 1)),
     ("direct", "fp16", (1, 5, 6, 7, 3), (3, 3, 3), (2, 2, 2), (1, 1, 1)),
     ("rows", "fp16", (1, 1, 19, 16, 3), (1, 7, 7), (1, 2, 2), (0, 3, 3)),
     ("rows", "bf16", (2, 5, 9, 8, 3), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
