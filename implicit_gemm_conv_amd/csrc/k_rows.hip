@@ -18,7 +18,9 @@
 //  * the filter, reordered and zero-padded to the group layout, is staged in
 //    LDS once per workgroup; workgroups are persistent and loop over tiles;
 //  * each wave computes 7 x 4 blocks of v_mfma_f32_16x16x32 (16 outputs x
-//    16 channels) per output row and stores runs of 4 channels (8 bytes);
+//    16 channels) per output row; with C_out of 16, 32 or 64 its row of
+//    outputs is one contiguous run of y, staged through LDS and stored as
+//    whole 16-byte pieces (else runs of 4 channels, 8 bytes);
 //  * the next tile's rows are loaded into registers while a tile computes,
 //    and two workgroups share a CU, so one's stores overlap the other's work.
 #include "conv_device.h"
@@ -207,7 +209,44 @@ __global__ __launch_bounds__(256, 2) void conv_rows_kernel(ConvParams p, RowsGeo
     }
 
     // ---- store: lane holds channels 16c + 4*fg + i of output ow0 + 16b + fr ----
-    if (oh < p.oh) {
+    // With C_out in {16, 32, 64} a wave's row of outputs is one contiguous run
+    // of y: it is staged through the wave's quarter of lds_in (free once every
+    // wave's reads of this tile are done), 32 outputs at a time with 16-byte
+    // piece k of output o at slot k ^ (o % pieces per output), and stored as
+    // whole 16-byte pieces, 1 KB of consecutive bytes per wave instruction.
+    const int ppo = p.cout / 8;              // 16-byte pieces per output
+    if (p.cout == 16 || p.cout == 32 || p.cout == 64) {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      char* ep = lds_in + wave * (kInBytes / 4);
+      const int ob = p.cout * 2;             // bytes per output
+      T* yrow = y + (int64_t)((nimg * p.od + od) * p.oh + oh) * p.ow * p.cout;
+#pragma unroll
+      for (int bp = 0; bp < (kSegBlocks + 1) / 2; ++bp) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int b = 2 * bp + bb;
+          if (b >= kSegBlocks) continue;
+          const int o = 16 * bb + fr;
+#pragma unroll
+          for (int c = 0; c < kNB; ++c) {
+            const int n = c * 16 + fg * 4;
+            if (n < p.cout) {
+              union { T h[4]; uint2 u; } pk;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[b][c][i]);
+              *(uint2*)(ep + o * ob + (((n >> 3) ^ (o & (ppo - 1))) * 16) + ((n >> 2) & 1) * 8) = pk.u;
+            }
+          }
+        }
+        const int nout = (2 * bp + 1 < kSegBlocks ? 32 : 16);
+        for (int l = lane * 16; l < nout * ob; l += 1024) {
+          const int o = l / ob, k = (l - o * ob) >> 4;
+          const uint4 v = *(const uint4*)(ep + o * ob + ((k ^ (o & (ppo - 1))) * 16));
+          const int ow = ow0 + 32 * bp + o;
+          if (oh < p.oh && ow < p.ow) *(uint4*)(yrow + (int64_t)ow * p.cout + k * 8) = v;
+        }
+      }
+    } else if (oh < p.oh) {
       T* yrow = y + (int64_t)((nimg * p.od + od) * p.oh + oh) * p.ow * p.cout;
 #pragma unroll
       for (int b = 0; b < kSegBlocks; ++b) {
