@@ -23,7 +23,8 @@ _lib = None
 class _Shape(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int64) for name in (
         "n", "d", "h", "w", "c_in", "c_out",
-        "k_d", "k_h", "k_w", "s_d", "s_h", "s_w", "p_d", "p_h", "p_w")]
+        "k_d", "k_h", "k_w", "s_d", "s_h", "s_w", "p_d", "p_h", "p_w",
+        "q_d", "q_h", "q_w", "e_d", "e_h", "e_w", "groups")]
 
 
 def _load():
@@ -40,6 +41,8 @@ def _load():
                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_out_extent.restype = ctypes.c_int64
         lib.oracle_out_extent.argtypes = [ctypes.c_int64] * 4
+        lib.oracle_out_extent_ex.restype = ctypes.c_int64
+        lib.oracle_out_extent_ex.argtypes = [ctypes.c_int64] * 6
         _lib = lib
     return _lib
 
@@ -57,30 +60,50 @@ def out_extent(size: int, k: int, s: int, p: int) -> int:
     return int(_load().oracle_out_extent(size, k, s, p))
 
 
+def out_extent_ex(size: int, k: int, s: int, p: int, q: int, e: int) -> int:
+    """floor((size + p + q - e*(k-1) - 1) / s) + 1 (low / high pads p / q, taps e apart)."""
+    return int(_load().oracle_out_extent_ex(size, k, s, p, q, e))
+
+
+def _pads(padding, dims):
+    """Per-dimension (low, high) pads from an int, a tuple of ints or a tuple of pairs."""
+    if isinstance(padding, int):
+        return ((padding, padding),) * dims
+    padding = tuple(padding)
+    assert len(padding) == dims
+    return tuple((int(p), int(p)) if isinstance(p, (int, np.integer)) else (int(p[0]), int(p[1]))
+                 for p in padding)
+
+
 def conv_fwd(x: np.ndarray, w: np.ndarray, stride=1, padding=0, rows=None,
-             return_macs: bool = False):
+             return_macs: bool = False, dilation=1, groups: int = 1):
     """Direct convolution, float64.
 
-    x: (N, H, W, C_in) or (N, D, H, W, C_in); w: (C_out, KH, KW, C_in) or
-    (C_out, KD, KH, KW, C_in); stride and padding: int or per-dimension tuple.
-    Returns y with shape (N, [D_out,] H_out, W_out, C_out), or, when ``rows``
-    (flat output-position indices) is given, an array (len(rows), C_out).
+    x: (N, H, W, C_in) or (N, D, H, W, C_in); w: (C_out, KH, KW, C_in/G) or
+    (C_out, KD, KH, KW, C_in/G); stride and dilation: int or per-dimension
+    tuple; padding: int, per-dimension int, or per-dimension (low, high) pair;
+    groups: G, dividing C_in and C_out.  Returns y with shape
+    (N, [D_out,] H_out, W_out, C_out), or, when ``rows`` (flat output-position
+    indices) is given, an array (len(rows), C_out).
     """
     x = np.ascontiguousarray(x, dtype=np.float64)
     w = np.ascontiguousarray(w, dtype=np.float64)
     dims = x.ndim - 2
-    assert dims in (2, 3) and w.ndim == x.ndim and w.shape[-1] == x.shape[-1]
+    assert dims in (2, 3) and w.ndim == x.ndim and w.shape[-1] * groups == x.shape[-1]
     st = _triple(stride, dims)
-    pd = _triple(padding, dims)
+    dl = _triple(dilation, dims)
+    pp = _pads(padding, dims)
     if dims == 2:
         x5 = x.reshape(x.shape[0], 1, *x.shape[1:])
         w5 = w.reshape(w.shape[0], 1, *w.shape[1:])
-        st, pd = (1,) + st, (0,) + pd
+        st, dl, pp = (1,) + st, (1,) + dl, ((0, 0),) + pp
     else:
         x5, w5 = x, w
     sh = _Shape(x5.shape[0], x5.shape[1], x5.shape[2], x5.shape[3], x5.shape[4], w5.shape[0],
-                w5.shape[1], w5.shape[2], w5.shape[3], *st, *pd)
-    outs = [out_extent(x5.shape[1 + i], w5.shape[1 + i], st[i], pd[i]) for i in range(3)]
+                w5.shape[1], w5.shape[2], w5.shape[3], *st, *(p[0] for p in pp),
+                *(p[1] for p in pp), *dl, groups)
+    outs = [out_extent_ex(x5.shape[1 + i], w5.shape[1 + i], st[i], pp[i][0], pp[i][1], dl[i])
+            for i in range(3)]
     if rows is None:
         y = np.zeros((x5.shape[0], *outs, w5.shape[0]), dtype=np.float64)
         rows_ptr, nrows = None, 0

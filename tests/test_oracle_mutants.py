@@ -21,12 +21,22 @@ MUTANTS = {
     "stride_on_tap": ("ow * s->s_w - s->p_w + kw", "ow - s->p_w + kw * s->s_w"),
     "ceil_extent": ("return span / s + 1;", "return (span + s - 1) / s + 1;"),
     "drops_first_column": ("if (w < 0 || w >= s->w) return 0.0;", "if (w < 1 || w >= s->w) return 0.0;"),
-    "drops_last_channel": ("for (int64_t c = 0; c < s->c_in; ++c)", "for (int64_t c = 0; c < s->c_in - 1; ++c)"),
+    "drops_last_channel": ("for (int64_t c = 0; c < cg; ++c)", "for (int64_t c = 0; c < cg - 1; ++c)"),
     "transposed_weight_taps": ("(((co * s->k_d + kd) * s->k_h + kh) * s->k_w + kw)",
                                "(((co * s->k_d + kd) * s->k_w + kw) * s->k_h + kh)"),
     "row_decode_mixup": ("const int64_t oh = (m / ow_n) % oh_n;", "const int64_t oh = (m / oh_n) % oh_n;"),
     "float_accumulator": ("double acc = 0.0;", "float acc = 0.0f;"),
     "drops_depth_padding": ("if (d < 0 || d >= s->d) return 0.0;", "if (d >= s->d) return 0.0;"),
+    # the variants: dilation, groups, asymmetric padding
+    "dilation_ignored_along_w": ("ow * s->s_w - s->p_w + kw * s->e_w", "ow * s->s_w - s->p_w + kw"),
+    "dilation_on_the_stride": ("od * s->s_d - s->p_d + kd * s->e_d", "od * s->s_d * s->e_d - s->p_d + kd"),
+    "dilation_missing_in_extent": ("int64_t span = in + p + q - (e * (k - 1) + 1);",
+                                   "int64_t span = in + p + q - k;"),
+    "high_pad_taken_as_low": ("int64_t span = in + p + q - (e * (k - 1) + 1);",
+                              "int64_t span = in + 2 * p - (e * (k - 1) + 1);"),
+    "group_channel_offset_dropped": ("g * cg + c)", "c)"),
+    "group_of_output_interleaved": ("const int64_t g = co / og;", "const int64_t g = co % s->groups;"),
+    "filter_channel_stride_ungrouped": ("* (s->c_in / s->groups) + c]", "* s->c_in + c]"),
 }
 
 

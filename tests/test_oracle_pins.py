@@ -254,3 +254,138 @@ def test_decode_formats_exactly():
                                   [1.0, 2.0**-133, (2 - 2.0**-7) * 2.0**127, -2.0])
     f32 = torch.tensor([1.0 + 2.0**-23, 2.0**-149], dtype=torch.float32)
     np.testing.assert_array_equal(oracle.to_float64(f32), [1.0 + 2.0**-23, 2.0**-149])
+
+
+# --- the variants: grouped, dilated, asymmetric padding ("Convolution variants worth
+#     knowing" on the tutorial page; pads per side as in the MLX benchmark tables) -----------
+
+def _stuffed(w, dil):
+    """The filter of taps `dil` apart as a dense filter with zeros in the gaps."""
+    cout, kd, kh, kw, c = w.shape
+    dd, dh, dw = dil
+    ws = np.zeros((cout, dd * (kd - 1) + 1, dh * (kh - 1) + 1, dw * (kw - 1) + 1, c))
+    ws[:, ::dd, ::dh, ::dw, :] = w
+    return ws
+
+
+DIL_CASES = [
+    ((5, 7, 9), (3, 3, 3), (1, 1, 1), (2, 2, 2), (2, 2, 2)),
+    ((4, 9, 8), (2, 3, 2), (1, 2, 1), (1, 3, 2), (3, 1, 2)),
+    ((1, 11, 10), (1, 3, 3), (1, 1, 2), (0, 2, 1), (1, 2, 3)),
+    ((6, 6, 6), (3, 2, 3), (2, 1, 1), (1, 0, 0), (2, 3, 1)),
+]
+
+
+@pytest.mark.parametrize("spatial,ks,st,pd,dil", DIL_CASES)
+def test_dilated_filter_equals_zero_stuffed_filter(spatial, ks, st, pd, dil):
+    """Taps e apart (a dilated filter) give exactly the convolution with the dense filter of
+    span e*(K-1)+1 that holds the taps at multiples of e and zeros between them."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((2, *spatial, 3))
+    w = rng.standard_normal((4, *ks, 3))
+    y = oracle.conv_fwd(x, w, st, pd, dilation=dil)
+    ref = oracle.conv_fwd(x, _stuffed(w, dil), st, pd)
+    assert y.shape == ref.shape
+    np.testing.assert_array_equal(y, ref)
+
+
+def _valid_taps_dilated(size, k, s, p, e, o):
+    """Brute force: taps t < k with 0 <= o*s - p + t*e < size."""
+    return sum(1 for t in range(k) if 0 <= o * s - p + t * e < size)
+
+
+@pytest.mark.parametrize("spatial,ks,st,pd,dil", DIL_CASES)
+def test_dilated_tap_count_brute_force(spatial, ks, st, pd, dil):
+    """x = 1, w = 1 on channel 0: every output counts its in-bounds dilated taps; output
+    extents are floor((in + 2p - e*(K-1) - 1)/s) + 1."""
+    x = np.ones((1, *spatial, 2))
+    w = np.zeros((2, *ks, 2))
+    w[..., 0] = 1.0
+    y = oracle.conv_fwd(x, w, st, pd, dilation=dil)
+    outs = [(spatial[i] + 2 * pd[i] - dil[i] * (ks[i] - 1) - 1) // st[i] + 1 for i in range(3)]
+    assert y.shape == (1, *outs, 2)
+    for od in range(outs[0]):
+        for oh in range(outs[1]):
+            for ow in range(outs[2]):
+                expect = (_valid_taps_dilated(spatial[0], ks[0], st[0], pd[0], dil[0], od)
+                          * _valid_taps_dilated(spatial[1], ks[1], st[1], pd[1], dil[1], oh)
+                          * _valid_taps_dilated(spatial[2], ks[2], st[2], pd[2], dil[2], ow))
+                assert np.all(y[0, od, oh, ow, :] == expect), (od, oh, ow)
+
+
+@pytest.mark.parametrize("groups,cin,cout", [(2, 6, 4), (3, 9, 6), (4, 8, 8), (5, 5, 10)])
+def test_groups_are_independent_convolutions_on_channel_slices(groups, cin, cout):
+    """G groups: output channels [g*C_out/G, (g+1)*C_out/G) are the plain convolution of input
+    channels [g*C_in/G, (g+1)*C_in/G) with their filters; the filter holds C_in/G channels."""
+    rng = np.random.default_rng(groups)
+    x = rng.standard_normal((2, 4, 5, 6, cin))
+    w = rng.standard_normal((cout, 3, 2, 3, cin // groups))
+    st, pd = (1, 2, 1), (1, 0, 2)
+    y = oracle.conv_fwd(x, w, st, pd, groups=groups)
+    cg, og = cin // groups, cout // groups
+    parts = [oracle.conv_fwd(x[..., g * cg:(g + 1) * cg], w[g * og:(g + 1) * og], st, pd)
+             for g in range(groups)]
+    np.testing.assert_array_equal(y, np.concatenate(parts, axis=-1))
+
+
+def test_depthwise_equals_per_channel_sums():
+    """Depthwise (G = C_in = C_out): y[..., c] = sum over taps of the shifted, strided input
+    channel c times w[c, tap, 0], built with numpy slicing."""
+    rng = np.random.default_rng(8)
+    c = 5
+    x = rng.standard_normal((2, 4, 6, 7, c))
+    w = rng.standard_normal((c, 3, 3, 2, 1))
+    st, pd = (1, 2, 1), (1, 1, 0)
+    y = oracle.conv_fwd(x, w, st, pd, groups=c)
+    outs = [oracle.out_extent(x.shape[1 + i], w.shape[1 + i], st[i], pd[i]) for i in range(3)]
+    xp = np.pad(x, ((0, 0), (pd[0], 8), (pd[1], 8), (pd[2], 8), (0, 0)))
+    ref = np.zeros((2, *outs, c))
+    for a in range(3):
+        for b in range(3):
+            for e in range(2):
+                sl = xp[:, a:a + outs[0] * st[0]:st[0], b:b + outs[1] * st[1]:st[1],
+                        e:e + outs[2] * st[2]:st[2], :]
+                ref += sl * w[:, a, b, e, 0]
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("pads", [((0, 2), (1, 0), (2, 1)), ((3, 0), (0, 3), (1, 2)), ((1, 1), (2, 0), (0, 0))])
+def test_asymmetric_padding_equals_explicitly_padded_input(pads):
+    """Low / high pads (p, q) give the unpadded convolution of the input with p zeros in
+    front and q behind along each dimension."""
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((2, 4, 5, 6, 3))
+    w = rng.standard_normal((4, 3, 3, 2, 3))
+    st = (1, 2, 2)
+    y = oracle.conv_fwd(x, w, st, pads)
+    xp = np.pad(x, ((0, 0), *pads, (0, 0)))
+    ref = oracle.conv_fwd(xp, w, st, 0)
+    assert y.shape == ref.shape
+    np.testing.assert_array_equal(y, ref)
+
+
+def test_all_variants_together_match_im2col_of_stuffed_padded_input():
+    """Groups, dilation and asymmetric pads at once against the independent im2col + GEMM
+    of each group's channel slice, with the filter zero-stuffed and the input padded
+    explicitly (so that path never sees a variant)."""
+    rng = np.random.default_rng(99)
+    for case in range(20):
+        g = int(rng.choice([1, 2, 3]))
+        cg, og = int(rng.integers(1, 4)), int(rng.integers(1, 3))
+        ks = [int(rng.integers(1, 4)) for _ in range(3)]
+        dl = [int(rng.integers(1, 3)) for _ in range(3)]
+        st = [int(rng.integers(1, 3)) for _ in range(3)]
+        pads = [(int(rng.integers(0, 3)), int(rng.integers(0, 3))) for _ in range(3)]
+        sp = [int(rng.integers(1, 6)) for _ in range(3)]
+        for i in range(3):
+            while sp[i] + sum(pads[i]) < dl[i] * (ks[i] - 1) + 1:
+                sp[i] += 1
+        x = rng.standard_normal((2, *sp, g * cg))
+        w = rng.standard_normal((g * og, *ks, cg))
+        y = oracle.conv_fwd(x, w, st, pads, dilation=dl, groups=g)
+        xp = np.pad(x, ((0, 0), *pads, (0, 0)))
+        ws = _stuffed(w, dl)
+        ref = np.concatenate([conv_im2col(xp[..., i * cg:(i + 1) * cg], ws[i * og:(i + 1) * og], st, (0, 0, 0))
+                              for i in range(g)], axis=-1)
+        assert y.shape == ref.shape, case
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12, err_msg=str(case))
