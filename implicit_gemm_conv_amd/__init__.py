@@ -35,6 +35,14 @@ class Desc(ctypes.Structure):
         "s_d", "s_h", "s_w", "p_d", "p_h", "p_w", "groups", "dtype")]
 
 
+class DescEx(ctypes.Structure):
+    """Mirror of convfwd_desc_ex (low / high padding, dilation, groups)."""
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "n", "d", "h", "w", "c_in", "c_out", "k_d", "k_h", "k_w",
+        "s_d", "s_h", "s_w", "p_d", "p_h", "p_w", "q_d", "q_h", "q_w",
+        "e_d", "e_h", "e_w", "groups", "dtype")]
+
+
 # Every entry point the header declares: (name, restype, argtypes).
 EXPORTS = [
     ("conv_out_shape", ctypes.c_int, [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_int64)]),
@@ -43,6 +51,12 @@ EXPORTS = [
                                 ctypes.c_void_p, ctypes.c_void_p]),
     ("conv_fwd_path", ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("conv_out_shape_ex", ctypes.c_int, [ctypes.POINTER(DescEx), ctypes.POINTER(ctypes.c_int64)]),
+    ("conv_select_path_ex", ctypes.c_int, [ctypes.POINTER(DescEx)]),
+    ("conv_fwd_ex", ctypes.c_int, [ctypes.POINTER(DescEx), ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p]),
+    ("conv_fwd_path_ex", ctypes.c_int, [ctypes.POINTER(DescEx), ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     ("conv_strerror", ctypes.c_char_p, [ctypes.c_int]),
     ("conv_path_name", ctypes.c_char_p, [ctypes.c_int]),
 ]
@@ -81,6 +95,37 @@ def _triple(v, dims, what):
     return v
 
 
+def _pairs(padding, dims):
+    """Per-dimension (low, high) pads from an int, a tuple of ints or a tuple of pairs."""
+    if isinstance(padding, int):
+        return ((padding, padding),) * dims
+    padding = tuple(padding)
+    if len(padding) != dims:
+        raise ValueError(f"padding needs {dims} entries, got {padding}")
+    return tuple((int(q), int(q)) if isinstance(q, int) else (int(q[0]), int(q[1])) for q in padding)
+
+
+def make_desc_ex(x_shape, w_shape, stride=1, padding=0, dilation=1, groups=1,
+                 dtype=torch.float16) -> DescEx:
+    """Extended descriptor for x (N,[D,]H,W,C_in) and w (C_out,[KD,]KH,KW,C_in/groups) shapes;
+    padding is an int, one int per dimension, or one (low, high) pair per dimension."""
+    dims = len(x_shape) - 2
+    if dims not in (2, 3) or len(w_shape) != len(x_shape):
+        raise ValueError(f"expected 4-D (2D) or 5-D (3D) x and w, got {x_shape}, {w_shape}")
+    st = _triple(stride, dims, "stride")
+    dl = _triple(dilation, dims, "dilation")
+    pp = _pairs(padding, dims)
+    if dims == 2:
+        x_shape = (x_shape[0], 1, *x_shape[1:])
+        w_shape = (w_shape[0], 1, *w_shape[1:])
+        st, dl, pp = (1, *st), (1, *dl), ((0, 0), *pp)
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return DescEx(x_shape[0], x_shape[1], x_shape[2], x_shape[3], x_shape[4], w_shape[0],
+                  w_shape[1], w_shape[2], w_shape[3], *st, *(q[0] for q in pp),
+                  *(q[1] for q in pp), *dl, groups, _DTYPES[dtype])
+
+
 def make_desc(x_shape, w_shape, stride=1, padding=0, dtype=torch.float16, groups=1) -> Desc:
     """Descriptor for x (N,[D,]H,W,C_in) and w (C_out,[KD,]KH,KW,C_in) shapes."""
     dims = len(x_shape) - 2
@@ -98,29 +143,32 @@ def make_desc(x_shape, w_shape, stride=1, padding=0, dtype=torch.float16, groups
                 w_shape[1], w_shape[2], w_shape[3], *st, *pd, groups, _DTYPES[dtype])
 
 
-def out_shape(x_shape, w_shape, stride=1, padding=0):
+def out_shape(x_shape, w_shape, stride=1, padding=0, dilation=1, groups=1):
     """Output shape (N,[D_out,]H_out,W_out,C_out) as the library computes it."""
-    d = make_desc(x_shape, w_shape, stride, padding)
+    d = make_desc_ex(x_shape, w_shape, stride, padding, dilation, groups)
     out = (ctypes.c_int64 * 5)()
-    _check(lib().conv_out_shape(ctypes.byref(d), out))
+    _check(lib().conv_out_shape_ex(ctypes.byref(d), out))
     shape = tuple(int(v) for v in out)
     return shape if len(x_shape) == 5 else (shape[0], *shape[2:])
 
 
-def select_path(x_shape, w_shape, stride=1, padding=0, dtype=torch.float16) -> str:
+def select_path(x_shape, w_shape, stride=1, padding=0, dtype=torch.float16, dilation=1,
+                groups=1) -> str:
     """Name of the path the library picks for this problem."""
-    d = make_desc(x_shape, w_shape, stride, padding, dtype)
-    return PATH_NAMES[_check(lib().conv_select_path(ctypes.byref(d)))]
+    d = make_desc_ex(x_shape, w_shape, stride, padding, dilation, groups, dtype)
+    return PATH_NAMES[_check(lib().conv_select_path_ex(ctypes.byref(d)))]
 
 
 def conv_fwd(x: torch.Tensor, w: torch.Tensor, stride=1, padding=0, out: torch.Tensor = None,
-             path: str = "auto") -> torch.Tensor:
+             path: str = "auto", dilation=1, groups: int = 1) -> torch.Tensor:
     """Channels-last convolution forward on the GPU.
 
-    x: (N,H,W,C_in) or (N,D,H,W,C_in); w: (C_out,KH,KW,C_in) or (C_out,KD,KH,KW,C_in);
-    same dtype (fp32, fp16 or bf16), same CUDA/HIP device.  Non-contiguous
-    inputs are made contiguous first.  Returns y (N,[D_out,]H_out,W_out,C_out)
-    in x's dtype, launched on the current stream of x's device (not synchronised).
+    x: (N,H,W,C_in) or (N,D,H,W,C_in); w: (C_out,KH,KW,C_in/groups) or
+    (C_out,KD,KH,KW,C_in/groups); same dtype (fp32, fp16 or bf16), same CUDA/HIP
+    device.  stride, dilation: int or per dimension; padding: int, per
+    dimension, or per dimension (low, high).  Non-contiguous inputs are made
+    contiguous first.  Returns y (N,[D_out,]H_out,W_out,C_out) in x's dtype,
+    launched on the current stream of x's device (not synchronised).
     """
     if not (x.is_cuda and w.is_cuda):
         raise ValueError("conv_fwd runs on the GPU only: x and w must be device tensors")
@@ -128,8 +176,8 @@ def conv_fwd(x: torch.Tensor, w: torch.Tensor, stride=1, padding=0, out: torch.T
         raise ValueError("x and w must share device and dtype")
     x = x.contiguous()
     w = w.contiguous()
-    d = make_desc(tuple(x.shape), tuple(w.shape), stride, padding, x.dtype)
-    shape = out_shape(tuple(x.shape), tuple(w.shape), stride, padding)
+    d = make_desc_ex(tuple(x.shape), tuple(w.shape), stride, padding, dilation, groups, x.dtype)
+    shape = out_shape(tuple(x.shape), tuple(w.shape), stride, padding, dilation, groups)
     if out is None:
         out = torch.empty(shape, dtype=x.dtype, device=x.device)
     elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous() \
@@ -137,8 +185,8 @@ def conv_fwd(x: torch.Tensor, w: torch.Tensor, stride=1, padding=0, out: torch.T
         raise ValueError(f"out must be a contiguous {x.dtype} tensor of shape {shape} on {x.device}")
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
-        _check(lib().conv_fwd_path(ctypes.byref(d), PATHS[path], x.data_ptr(), w.data_ptr(),
-                                   out.data_ptr(), stream))
+        _check(lib().conv_fwd_path_ex(ctypes.byref(d), PATHS[path], x.data_ptr(), w.data_ptr(),
+                                      out.data_ptr(), stream))
     return out
 
 

@@ -32,16 +32,18 @@ template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return
 // Output position m = ((n*od + z)*oh + y)*ow + x.  Gives the input origin of
 // its window (the position of tap (0,0,0), possibly in the padding) as an
 // element offset into x, and the per-dimension validity masks: bit t of md is
-// set iff input depth z*sd - pd + t lies inside [0, d), likewise mh and mw.
+// set iff input depth z*sd - pd + t*ed lies inside [0, d), likewise mh and mw.
 struct RowInfo {
   int base;      // element offset of the window origin (may be negative or past the end)
   uint32_t md, mh, mw;
 };
 
-// Bits t in [max(0, -i0), min(k, size - i0)) set; k <= 16 (so every shift is < 32).
-__device__ __forceinline__ uint32_t dim_mask(int i0, int k, int size) {
-  const int lo = max(0, -i0);
-  const int hi = min(k, size - i0);
+// Bits t with 0 <= i0 + t*e < size set, t < k <= 16 (so every shift is < 32):
+// the taps t in [ceil(-i0 / e), floor((size - 1 - i0) / e)] of a filter whose
+// taps are e positions apart.
+__device__ __forceinline__ uint32_t dim_mask(int i0, int k, int size, int e = 1) {
+  const int lo = i0 >= 0 ? 0 : (-i0 + e - 1) / e;
+  const int hi = i0 > size - 1 ? 0 : min(k, (size - 1 - i0) / e + 1);
   if (hi <= lo) return 0u;
   return ((1u << hi) - 1u) & ~((1u << lo) - 1u);
 }
@@ -62,9 +64,9 @@ __device__ __forceinline__ RowInfo decode_row(const ConvParams& p, int m) {
   const int y0 = yo * p.sh - p.ph;
   const int x0 = xo * p.sw - p.pw;
   r.base = n * p.xs_n + z0 * p.xs_d + y0 * p.xs_h + x0 * p.xs_w;
-  r.md = dim_mask(z0, p.kd, p.d);
-  r.mh = dim_mask(y0, p.kh, p.h);
-  r.mw = dim_mask(x0, p.kw, p.w);
+  r.md = dim_mask(z0, p.kd, p.d, p.ed);
+  r.mh = dim_mask(y0, p.kh, p.h, p.eh);
+  r.mw = dim_mask(x0, p.kw, p.w, p.ew);
   return r;
 }
 

@@ -16,13 +16,19 @@ struct ConvParams {
   int cin, cout;           // channels
   int kd, kh, kw;          // filter extents
   int sd, sh, sw;          // strides
-  int pd, ph, pw;          // zero padding, both sides
+  int pd, ph, pw;          // zero padding on the low side (the high side only sets od, oh, ow)
+  int ed, eh, ew;          // filter dilation: tap t sits t*e positions past the window origin
+  int groups;              // channel groups: output channel co reads the cin_g input
+  int cin_g, cout_g;       //   channels of group co / cout_g (cin = groups * cin_g)
   int od, oh, ow;          // output extents
   int M;                   // GEMM rows: n * od * oh * ow
   int ntaps;               // kd * kh * kw
-  int K;                   // GEMM depth: ntaps * cin (the filter's row length)
+  int K;                   // GEMM depth of one group: ntaps * cin_g (the filter's row length)
   int xs_w, xs_h, xs_d, xs_n;  // element strides of x along w, h, d, n (xs_w == cin)
 };
+
+// The plain convolution: one group, undilated filter.
+inline bool plain(const ConvParams& p) { return p.groups == 1 && p.ed == 1 && p.eh == 1 && p.ew == 1; }
 
 enum DType { kF32 = 0, kF16 = 1, kBF16 = 2 };
 

@@ -420,7 +420,7 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
 }  // namespace
 
 bool brick_accepts(const ConvParams& p, int dtype) {
-  if (!(dtype == kF16 || dtype == kBF16)) return false;
+  if (!(dtype == kF16 || dtype == kBF16) || !plain(p)) return false;
   if (p.cin % 16 != 0 || p.cout % 4 != 0 || p.ntaps < 4) return false;
   if (p.kd > 16 || p.kh > 16 || p.kw > 16) return false;
   BrickGeom g;

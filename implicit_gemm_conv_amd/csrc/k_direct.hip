@@ -2,9 +2,9 @@
 //
 // Each thread walks its window tap by tap and channel by channel with fp32
 // FMAs, skipping taps that fall in the zero padding.  It accepts every problem
-// the descriptor can express (any filter size, any channel count, all three
-// dtypes) and serves as the always-available fallback and as a layout-free
-// cross-check of the MFMA paths.
+// the descriptor can express (any filter size, any channel count, groups,
+// dilation, all three dtypes) and serves as the always-available fallback and
+// as a layout-free cross-check of the MFMA paths.
 #include "conv_device.h"
 
 namespace convfwd {
@@ -24,20 +24,21 @@ __global__ __launch_bounds__(256) void conv_direct_kernel(ConvParams p, const T*
   const int zo = t % p.od;
   const int n = t / p.od;
   const T* wrow = w + (int64_t)co * p.K;
+  const int c0 = (co / p.cout_g) * p.cin_g;   // first input channel of this output's group
   float acc = 0.f;
   for (int a = 0; a < p.kd; ++a) {
-    const int zi = zo * p.sd - p.pd + a;
+    const int zi = zo * p.sd - p.pd + a * p.ed;
     if (zi < 0 || zi >= p.d) continue;
     for (int b = 0; b < p.kh; ++b) {
-      const int yi = yo * p.sh - p.ph + b;
+      const int yi = yo * p.sh - p.ph + b * p.eh;
       if (yi < 0 || yi >= p.h) continue;
       for (int e = 0; e < p.kw; ++e) {
-        const int xi = xo * p.sw - p.pw + e;
+        const int xi = xo * p.sw - p.pw + e * p.ew;
         if (xi < 0 || xi >= p.w) continue;
         const T* xp = x + (int64_t)n * p.xs_n + (int64_t)zi * p.xs_d + (int64_t)yi * p.xs_h +
-                      (int64_t)xi * p.xs_w;
-        const T* wp = wrow + ((a * p.kh + b) * p.kw + e) * p.cin;
-        for (int c = 0; c < p.cin; ++c) acc = fmaf(to_f32(xp[c]), to_f32(wp[c]), acc);
+                      (int64_t)xi * p.xs_w + c0;
+        const T* wp = wrow + ((a * p.kh + b) * p.kw + e) * p.cin_g;
+        for (int c = 0; c < p.cin_g; ++c) acc = fmaf(to_f32(xp[c]), to_f32(wp[c]), acc);
       }
     }
   }

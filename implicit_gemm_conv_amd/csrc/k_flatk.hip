@@ -205,7 +205,7 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
 
 bool flatk_accepts(const ConvParams& p, int dtype) {
   (void)dtype;
-  return p.kd <= 16 && p.kh <= 16 && p.kw <= 16;
+  return plain(p) && p.kd <= 16 && p.kh <= 16 && p.kw <= 16;
 }
 
 hipError_t launch_flatk(const ConvParams& p, int dtype, const void* x, const void* w, void* y,

@@ -114,7 +114,15 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int m0 = (tile / tiles_n) * BM;
-  const int n0 = (tile % tiles_n) * BN;
+  // Column tiles never straddle a channel group: tile tn covers output
+  // channels n0 .. of group g = tn / tpg, which reads input channels
+  // g*cin_g .. (g+1)*cin_g - 1; columns stop at the group's end n_end.
+  const int tpg = (p.cout_g + BN - 1) / BN;   // column tiles per group
+  const int tn = tile % tiles_n;
+  const int grp = tn / tpg;
+  const int n0 = grp * p.cout_g + (tn - grp * tpg) * BN;
+  const int n_end = (grp + 1) * p.cout_g;
+  const int c_grp = grp * p.cin_g;
 
   // Loader geometry: a wave's load instruction fills RPI consecutive tile
   // rows (1 KB of LDS); lane l writes row l / CPR, physical chunk l % CPR,
@@ -132,22 +140,22 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
     ri[i] = decode_row(p, m0 + i * RPR + lrow);
-    ri[i].base = (ri[i].base + lchunk * 8) * 2;   // byte offset of this lane's chunk at tap 0
+    ri[i].base = (ri[i].base + c_grp + lchunk * 8) * 2;   // byte offset of this lane's chunk at tap 0
   }
   uint32_t boff[B_LOADS];
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j) {
     const int n = n0 + j * RPR + lrow;
-    boff[j] = n < p.cout ? (uint32_t)((n * p.K + lchunk * 8) * 2) : kOutOfRange;
+    boff[j] = n < n_end ? (uint32_t)((n * p.K + lchunk * 8) * 2) : kOutOfRange;
   }
 
-  const int S = (p.cin / BK) * p.ntaps;
+  const int S = (p.cin_g / BK) * p.ntaps;
   int ic = 0, ikd = 0, ikh = 0, ikw = 0;  // (channel chunk, tap) of the next step to issue
 
   auto issue = [&](int stage) {
     char* sa = smem + stage * STAGE_BYTES;
     char* sb = sa + BM * ROWB;
-    const int xoff = (ikd * p.xs_d + ikh * p.xs_h + ikw * p.xs_w + ic * BK) * 2;
+    const int xoff = (ikd * p.ed * p.xs_d + ikh * p.eh * p.xs_h + ikw * p.ew * p.xs_w + ic * BK) * 2;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const uint32_t off =
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xr, (lds_ptr_t)(sa + (i * RPR + wave * RPI) * ROWB), 16, off, 0, 0, 0);
     }
-    const uint32_t woff = (uint32_t)((((ikd * p.kh + ikh) * p.kw + ikw) * p.cin + ic * BK) * 2);
+    const uint32_t woff = (uint32_t)((((ikd * p.kh + ikh) * p.kw + ikw) * p.cin_g + ic * BK) * 2);
 #pragma unroll
     for (int j = 0; j < B_LOADS; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   constexpr int ORPI = 64 / OCH;        // output rows per wave instruction
-  const bool whole16 = (p.cout & 7) == 0;
+  const bool whole16 = (p.cout & 7) == 0 && (p.cout_g & 7) == 0;   // 16-byte stores stay aligned
 #pragma unroll 4
   for (int i = 0; i < BM / (4 * ORPI); ++i) {
     const int row = (4 * i + wave) * ORPI + lane / OCH, k = lane % OCH;
@@ -246,14 +254,14 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
     const int n = n0 + k * 8;
     if (m < p.M) {
       T* dst = y + (int64_t)m * p.cout + n;
-      if (n + 8 <= p.cout) {
+      if (n + 8 <= n_end) {
         if (whole16) {
           *(uint4*)dst = v;
         } else {
           *(uint2*)dst = make_uint2(v.x, v.y);
           *(uint2*)(dst + 4) = make_uint2(v.z, v.w);
         }
-      } else if (n + 4 <= p.cout) {
+      } else if (n + 4 <= n_end) {
         *(uint2*)dst = make_uint2(v.x, v.y);
       }
     }
@@ -264,7 +272,7 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
 template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int MF>
 hipError_t launch_cfg(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   const int tiles_m = (p.M + BM - 1) / BM;
-  const int tiles_n = (p.cout + BN - 1) / BN;
+  const int tiles_n = p.groups * ((p.cout_g + BN - 1) / BN);
   const uint32_t xb = (uint32_t)((int64_t)p.n * p.xs_n * 2);
   const uint32_t wb = (uint32_t)((int64_t)p.cout * p.K * 2);
   hipLaunchKernelGGL((conv_main_kernel<T, BM, BN, BK, WM, WN, STAGES, OCC, MF>),
@@ -315,11 +323,11 @@ hipError_t launch_variant(int v, const ConvParams& p, const void* x, const void*
 template <typename T>
 hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
 #ifdef CONVFWD_MAIN_VARIANT
-  if (p.cin % variant_bk(CONVFWD_MAIN_VARIANT) == 0)
+  if (p.cin_g % variant_bk(CONVFWD_MAIN_VARIANT) == 0)
     return launch_variant<T>(CONVFWD_MAIN_VARIANT, p, x, w, y, s);
 #endif
-  const bool bk64 = p.cin % 64 == 0;
-  const long tiles_256 = (long)((p.M + 255) / 256) * ((p.cout + 127) / 128);
+  const bool bk64 = p.cin_g % 64 == 0;
+  const long tiles_256 = (long)((p.M + 255) / 256) * p.groups * ((p.cout_g + 127) / 128);
   if (tiles_256 >= 256) return launch_variant<T>(bk64 ? 4 : 3, p, x, w, y, s);
   return launch_variant<T>(bk64 ? 9 : 8, p, x, w, y, s);
 }
@@ -327,7 +335,7 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
 }  // namespace
 
 bool main_accepts(const ConvParams& p, int dtype) {
-  return (dtype == kF16 || dtype == kBF16) && p.cin % 32 == 0 && p.cout % 4 == 0 && p.kd <= 16 &&
+  return (dtype == kF16 || dtype == kBF16) && p.cin_g % 32 == 0 && p.cout_g % 4 == 0 && p.kd <= 16 &&
          p.kh <= 16 && p.kw <= 16;
 }
 

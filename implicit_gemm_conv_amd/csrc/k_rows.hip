@@ -311,7 +311,7 @@ bool make_geom(const ConvParams& p, RowsGeom* g) {
 }  // namespace
 
 bool rows_accepts(const ConvParams& p, int dtype) {
-  if (!(dtype == kF16 || dtype == kBF16)) return false;
+  if (!(dtype == kF16 || dtype == kBF16) || !plain(p)) return false;
   if (p.cin >= 16 || p.cin * p.kw > 32 || p.cout > 64) return false;
   if ((p.w * p.cin) % 8 != 0) return false;       // input rows start on 16-byte boundaries
   RowsGeom g;

@@ -1,5 +1,6 @@
 // k_runs.hip -- implicit GEMM for any C_in (the unaligned-channel tail path)
-// and fp32, reading the im2col matrix as contiguous runs.
+// and fp32, reading the im2col matrix as contiguous runs; also the grouped and
+// dilated variants.
 //
 // With K ordered (kd, kh, kw, c), the K_w * C_in columns of one (kd, kh) form
 // a run that is contiguous in memory on both sides of the product: in x the
@@ -15,6 +16,8 @@
 // that would start before x or reach past the end of a tensor (only possible
 // on its first and last lines) are fetched element by element, since the
 // buffer range check drops any dword that is not wholly inside the tensor.
+// Grouped or w-dilated problems use shorter runs: the C_in/G channels of one
+// tap, a group's slice of one window position.
 //
 // Pipeline: the pieces of DEPTH steps are in flight in registers at once; each
 // step's pieces are masked and written to a double-buffered LDS tile (rows
@@ -118,15 +121,25 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int m0 = (tile / tiles_n) * BM;
-  const int n0 = (tile % tiles_n) * BN;
+  // column tiles never straddle a channel group (see launch_cfg)
+  const int tpg = (p.cout_g + BN - 1) / BN;
+  const int tn = tile % tiles_n;
+  const int grp = tn / tpg;
+  const int n0 = grp * p.cout_g + (tn - grp * tpg) * BN;
+  const int n_end = (grp + 1) * p.cout_g;
   const __amdgpu_buffer_rsrc_t xr =
       __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, x_bytes, kRawBufferFlags);
   const __amdgpu_buffer_rsrc_t wr =
       __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, w_bytes, kRawBufferFlags);
 
-  const int run = p.kw * p.cin;                // columns of one (kd, kh)
+  // A run is the K_w * C_in columns of one (kd, kh) when the whole window row
+  // is contiguous (one group, undilated along w); otherwise the C_in/G
+  // columns of one tap (kd, kh, kw).
+  const bool wide = p.groups == 1 && p.ew == 1;
+  const int run = wide ? p.kw * p.cin : p.cin_g;
+  const int nkw = wide ? 1 : p.kw;             // runs per (kd, kh)
   const int sps = (run + kBK - 1) / kBK;       // steps per run
-  const int S = p.kd * p.kh * sps;
+  const int S = p.kd * p.kh * nkw * sps;
 
   // A pieces: thread piece i -> tile row, piece q; the run of that output row
   // at (kd, kh) = (0, 0) starts at element a_e[i] - q * EPC, and its columns
@@ -134,6 +147,7 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   // inside the input along w.
   int a_e[A_PER], a_lo[A_PER], a_hi[A_PER];
   uint32_t a_dh[A_PER];   // depth-tap bits | height-tap bits << 16
+  uint32_t a_w[A_PER];    // width-tap bits (per-tap runs) or all ones (whole window rows)
   int a_ldsoff[A_PER];
 #pragma unroll
   for (int i = 0; i < A_PER; ++i) {
@@ -141,10 +155,11 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
     const RowInfo ri = decode_row(p, m0 + row);
     const int lo_w = ri.mw ? __builtin_ctz(ri.mw) : 0;
     const int hi_w = ri.mw ? 32 - __builtin_clz(ri.mw) : 0;
-    a_e[i] = ri.base + q * EPC;
-    a_lo[i] = lo_w * p.cin - q * EPC;
-    a_hi[i] = hi_w * p.cin - q * EPC;
+    a_e[i] = ri.base + grp * p.cin_g + q * EPC;
+    a_lo[i] = (wide ? lo_w * p.cin : 0) - q * EPC;
+    a_hi[i] = (wide ? hi_w * p.cin : p.cin_g) - q * EPC;
     a_dh[i] = ri.md | (ri.mh << 16);
+    a_w[i] = wide ? 0xffffffffu : ri.mw;
     a_ldsoff[i] = row * ROWB + q * 16;
   }
   // B pieces: filter row n0 + brow, piece bq; columns past the run are zero.
@@ -154,7 +169,7 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   for (int j = 0; j < B_PER; ++j) {
     const int c = tid + 256 * j, brow = c / CPR, bq = c % CPR;
     const int co = n0 + brow;
-    b_ok[j] = c < B_PIECES && co < p.cout;
+    b_ok[j] = c < B_PIECES && co < n_end;
     b_e[j] = co * p.K + bq * EPC;
     b_hi[j] = run - bq * EPC;
     b_ldsoff[j] = BM * ROWB + brow * ROWB + bq * 16;
@@ -163,15 +178,15 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   // Loads of the step (kd, kh, k0) into register slot `slot`; steps past the
   // end load nothing.
   u4 ra[DEPTH][A_PER], rb[DEPTH][B_PER];
-  int l_kd = 0, l_kh = 0, l_k0 = 0, l_step = 0;
+  int l_kd = 0, l_kh = 0, l_kw = 0, l_k0 = 0, l_step = 0;
   int s_k0[DEPTH];   // column offset of the step in each slot (for the masks)
   auto load_step = [&](int slot) {
     const bool live = l_step < S;
-    const int xo = l_kd * p.xs_d + l_kh * p.xs_h + l_k0;
-    const int wo = (l_kd * p.kh + l_kh) * run + l_k0;
+    const int xo = l_kd * p.ed * p.xs_d + l_kh * p.eh * p.xs_h + l_kw * p.ew * p.xs_w + l_k0;
+    const int wo = ((l_kd * p.kh + l_kh) * nkw + l_kw) * run + l_k0;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      const bool ok = live && ((a_dh[i] >> l_kd) & (a_dh[i] >> (16 + l_kh)) & 1u);
+      const bool ok = live && ((a_dh[i] >> l_kd) & (a_dh[i] >> (16 + l_kh)) & (a_w[i] >> l_kw) & 1u);
       ra[slot][i] = load_piece<EB>(xr, a_e[i] + xo, ok, a_lo[i] - l_k0, a_hi[i] - l_k0, x_bytes);
     }
 #pragma unroll
@@ -181,9 +196,12 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
     l_k0 += kBK;
     if (l_k0 >= run) {
       l_k0 = 0;
-      if (++l_kh == p.kh) {
-        l_kh = 0;
-        ++l_kd;
+      if (++l_kw == nkw) {
+        l_kw = 0;
+        if (++l_kh == p.kh) {
+          l_kh = 0;
+          ++l_kd;
+        }
       }
     }
     ++l_step;
@@ -233,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // loads past the end
 
   // Epilogue: lane holds D[n = 4*fg + i][m = fr] of each 16x16 block.
-  const bool vec_ok = (p.cout & 3) == 0;
+  const bool vec_ok = (p.cout & 3) == 0 && (p.cout_g & 3) == 0;
 #pragma unroll
   for (int a = 0; a < FM; ++a) {
     const int m = m0 + wave * TM + a * 16 + fr;
@@ -242,7 +260,7 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
       const int n = n0 + b * 16 + fg * 4;
-      if (vec_ok && n + 3 < p.cout) {
+      if (vec_ok && n + 3 < n_end) {
         if constexpr (EB == 2) {
           union { T h[4]; uint2 u; } pk;
 #pragma unroll
@@ -254,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (n + i < p.cout) yrow[n + i] = from_f32<T>(acc[a][b][i]);
+          if (n + i < n_end) yrow[n + i] = from_f32<T>(acc[a][b][i]);
       }
     }
   }
@@ -269,7 +287,7 @@ template <typename T, int BM, int BN>
 hipError_t launch_cfg(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   constexpr int DEPTH = BM == 64 && (sizeof(T) == 2 || BN < 128) ? 8 : 2;
   const int tiles_m = (p.M + BM - 1) / BM;
-  const int tiles_n = (p.cout + BN - 1) / BN;
+  const int tiles_n = p.groups * ((p.cout_g + BN - 1) / BN);
   const int xb = (int)((int64_t)p.n * p.xs_n * sizeof(T));
   const int wb = (int)((int64_t)p.cout * p.K * sizeof(T));
   hipLaunchKernelGGL((conv_runs_kernel<T, BM, BN, DEPTH>), dim3(tiles_m * tiles_n), dim3(256), 0, s, p,
@@ -277,15 +295,15 @@ hipError_t launch_cfg(const ConvParams& p, const void* x, const void* w, void* y
   return hipGetLastError();
 }
 
-// Column tile: the smallest of 32, 48, 64, 80, 128 that holds C_out (128 and
-// several column tiles beyond that); row tile 128 when that still gives a few
+// Column tile: the smallest of 32, 48, 64, 80, 128 that holds one group's
+// C_out/G (128 and several column tiles beyond that); row tile 128 when that still gives a few
 // hundred tiles, else 64 (fp32 always 64).
 template <typename T, int BM>
 hipError_t launch_bn(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
-  if (p.cout <= 32) return launch_cfg<T, BM, 32>(p, x, w, y, s);
-  if (p.cout <= 48) return launch_cfg<T, BM, 48>(p, x, w, y, s);
-  if (p.cout <= 64) return launch_cfg<T, BM, 64>(p, x, w, y, s);
-  if (p.cout <= 80) return launch_cfg<T, BM, 80>(p, x, w, y, s);
+  if (p.cout_g <= 32) return launch_cfg<T, BM, 32>(p, x, w, y, s);
+  if (p.cout_g <= 48) return launch_cfg<T, BM, 48>(p, x, w, y, s);
+  if (p.cout_g <= 64) return launch_cfg<T, BM, 64>(p, x, w, y, s);
+  if (p.cout_g <= 80) return launch_cfg<T, BM, 80>(p, x, w, y, s);
   return launch_cfg<T, BM, 128>(p, x, w, y, s);
 }
 

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
       const int z0 = od * p.sd - p.pd, y0 = oh * p.sh - p.ph;
       const int iw = ow0 - p.pw + o;
       if (iw >= 0 && iw < p.w) {
-        mask = dim_mask(z0, p.kd, p.d) | (dim_mask(y0, p.kh, p.h) << 16);
+        mask = dim_mask(z0, p.kd, p.d, p.ed) | (dim_mask(y0, p.kh, p.h, p.eh) << 16);
         base = (uint32_t)(((n * p.xs_n + z0 * p.xs_d + y0 * p.xs_h + iw * p.xs_w) + c * 8) * 2);
       }
     }
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
   auto issue_a_part = [&](int q0, int q1) {
     char* sa = smem + a_slot * kStripBytes;
     const uint32_t live = a_ic < nchunks ? ~0u : 0u;
-    const uint32_t xoff = (uint32_t)((a_kd * p.xs_d + a_kh * p.xs_h + a_ic * 32) * 2);
+    const uint32_t xoff = (uint32_t)((a_kd * p.ed * p.xs_d + a_kh * p.eh * p.xs_h + a_ic * 32) * 2);
 #pragma unroll
     for (int q = q0; q < q1; ++q) {
       const bool ok = (((a_mask[q] & live) >> a_kd) & (a_mask[q] >> (16 + a_kh)) & 1u) != 0u;
@@ -389,7 +389,8 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
 }  // namespace
 
 bool strip_accepts(const ConvParams& p, int dtype) {
-  return (dtype == kF16 || dtype == kBF16) && p.cin % 32 == 0 && p.cout % 4 == 0 && p.sw == 1 &&
+  return (dtype == kF16 || dtype == kBF16) && p.groups == 1 && p.ew == 1 && p.cin % 32 == 0 &&
+         p.cout % 4 == 0 && p.sw == 1 &&
          p.ow % kSeg == 0 && p.kw <= kMaxKW && p.kd <= 16 && p.kh <= 16;
 }
 

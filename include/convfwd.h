@@ -13,14 +13,22 @@
  *
  * with X the input extended by zeros outside its extent.  The filter is not
  * flipped (the tutorial's worked example fixes the orientation).  Output
- * extents are floor((in + 2p - k)/s) + 1.  The result is computed as an
+ * extents are floor((in + 2p - k)/s) + 1.
+ *
+ * The variants the tutorial lists among "Convolution variants worth knowing"
+ * take the same sum and are reached through convfwd_desc_ex: grouped
+ * (channels split into G groups; output channel co reads only the C_in/G input
+ * channels of its group g = co / (C_out/G), X's channel g*C_in/G + c), dilated
+ * (tap t sits t*e positions past the window origin, "gaps in the kernel"), and
+ * padded differently on the low (p) and high (q) side of a dimension; then
+ * extents are floor((in + p + q - e*(k-1) - 1)/s) + 1.  The result is computed as an
  * implicit GEMM (tutorial section 5, "Alternatives"): M = N*D_out*H_out*W_out
  * rows, N_gemm = C_out columns, K = C_in*K_d*K_h*K_w, with the im2col operand
  * addressed on the fly inside the kernel and never stored.
  *
  * Layouts (all dense, innermost dimension last, no padding between rows):
  *   x  (N, D, H, W, C_in)                   channels-last input
- *   w  (C_out, K_d, K_h, K_w, C_in)         filter, C_in fastest
+ *   w  (C_out, K_d, K_h, K_w, C_in/G)       filter, C_in/G fastest (G = 1 unless grouped)
  *   y  (N, D_out, H_out, W_out, C_out)      channels-last output, same dtype as x
  * A 2D problem is the 3D one with d = k_d = s_d = 1 and p_d = 0.
  *
@@ -57,8 +65,9 @@ typedef enum {
 enum {
   CONVFWD_OK = 0,
   CONVFWD_ERR_NULL = -1,        /* a required pointer is NULL */
-  CONVFWD_ERR_BAD_DESC = -2,    /* a non-positive extent, stride < 1, pad < 0, or an empty output */
-  CONVFWD_ERR_UNSUPPORTED = -3, /* groups != 1, unknown dtype, or a path that cannot take this problem */
+  CONVFWD_ERR_BAD_DESC = -2,    /* a non-positive extent, stride or dilation < 1, pad < 0, groups < 1
+                                   or not dividing C_in and C_out, or an empty output */
+  CONVFWD_ERR_UNSUPPORTED = -3, /* unknown dtype, or a path that cannot take this problem */
   CONVFWD_ERR_TOO_LARGE = -4,   /* a tensor of 2^31 bytes or more, or M >= 2^31 */
   CONVFWD_ERR_ALIAS = -5,       /* y's byte range overlaps x or w */
   CONVFWD_ERR_LAUNCH = -6       /* the HIP runtime refused the launch */
@@ -68,18 +77,18 @@ enum {
  * testing every path on every shape it accepts). */
 typedef enum {
   CONVFWD_PATH_AUTO = 0,
-  CONVFWD_PATH_MAIN = 1,   /* fp16/bf16, C_in % 32 == 0, C_out % 4 == 0, filter <= 16 per dim:
+  CONVFWD_PATH_MAIN = 1,   /* fp16/bf16, C_in/G % 32 == 0, C_out/G % 4 == 0, filter <= 16 per dim:
                               16-byte channels-last loads straight into LDS, MFMA */
-  CONVFWD_PATH_FLATK = 2,  /* any C_in (the unaligned-channel tail path), filter <= 16 per dim:
-                              element-granular gathers over the flattened (tap, channel) axis, MFMA */
-  CONVFWD_PATH_ROWS = 3,   /* fp16/bf16 tiny C_in (C_in * K_w <= 64, 2D or 3D): whole input rows
-                              staged in LDS, MFMA */
+  CONVFWD_PATH_FLATK = 2,  /* any C_in, filter <= 16 per dim, G = 1, undilated: element-granular
+                              gathers over the flattened (tap, channel) axis, MFMA */
+  CONVFWD_PATH_ROWS = 3,   /* fp16/bf16 tiny C_in (C_in * K_w <= 32, 2D or 3D), G = 1, undilated:
+                              whole input rows staged in LDS, MFMA */
   CONVFWD_PATH_DIRECT = 4, /* any problem: one thread per output, fp32 FMA (slow, simple) */
-  CONVFWD_PATH_BRICK = 5,  /* fp16/bf16, C_in % 16 == 0, C_out % 4 == 0, >= 4 taps, filter <= 16
+  CONVFWD_PATH_BRICK = 5,  /* fp16/bf16, G = 1, undilated, C_in % 16 == 0, C_out % 4 == 0, >= 4 taps, filter <= 16
                               per dim and a brick that fits: the input brick of a box of up to
                               512 outputs staged in LDS per 16-channel chunk, every tap read
                               from it, MFMA */
-  CONVFWD_PATH_STRIP = 6,  /* fp16/bf16, C_in % 32 == 0, C_out % 4 == 0, stride 1 along w,
+  CONVFWD_PATH_STRIP = 6,  /* fp16/bf16, G = 1, C_in % 32 == 0, C_out % 4 == 0, stride and dilation 1 along w,
                               W_out % 32 == 0, K_w <= 5, K_d, K_h <= 16: per (channel chunk,
                               kd, kh) one input strip per 32-output w-segment staged in LDS,
                               all K_w taps read from it, 512 x 128 tiles, MFMA */
@@ -95,9 +104,24 @@ typedef struct {
   int32_t k_d, k_h, k_w;     /* filter extents (k_d = 1 for 2D) */
   int32_t s_d, s_h, s_w;     /* strides, >= 1 */
   int32_t p_d, p_h, p_w;     /* zero padding added on both sides, >= 0 */
-  int32_t groups;            /* must be 1 */
+  int32_t groups;            /* channel groups G >= 1 dividing c_in and c_out (1: plain) */
   int32_t dtype;             /* convfwd_dtype; x, w and y share it */
 } convfwd_desc;
+
+/* Extended descriptor: as convfwd_desc, plus the padding of the high side of
+ * each dimension and the filter dilation.  A convfwd_desc is the extended one
+ * with q_* = p_* and e_* = 1. */
+typedef struct {
+  int32_t n, d, h, w;        /* input batch and spatial extents (d = 1 for 2D) */
+  int32_t c_in, c_out;       /* channels */
+  int32_t k_d, k_h, k_w;     /* filter extents (taps per dimension) */
+  int32_t s_d, s_h, s_w;     /* strides, >= 1 */
+  int32_t p_d, p_h, p_w;     /* zero padding before the first element (low side), >= 0 */
+  int32_t q_d, q_h, q_w;     /* zero padding after the last element (high side), >= 0 */
+  int32_t e_d, e_h, e_w;     /* filter dilation, >= 1: tap t sits t*e positions past the origin */
+  int32_t groups;            /* channel groups G >= 1 dividing c_in and c_out */
+  int32_t dtype;             /* convfwd_dtype; x, w and y share it */
+} convfwd_desc_ex;
 
 /* Output shape (N, D_out, H_out, W_out, C_out) into out[5].  Host only; never
  * touches the GPU.  Returns CONVFWD_OK or a validation error. */
@@ -118,6 +142,15 @@ int conv_fwd(const convfwd_desc* desc, const void* x, const void* w, void* y, vo
  * cannot take the problem. */
 int conv_fwd_path(const convfwd_desc* desc, int path, const void* x, const void* w, void* y,
                   void* stream);
+
+/* The four calls above for an extended descriptor (same arguments, same
+ * rules; every path takes groups, dilation and asymmetric padding except as
+ * its comment in convfwd_path restricts). */
+int conv_out_shape_ex(const convfwd_desc_ex* desc, int64_t out[5]);
+int conv_select_path_ex(const convfwd_desc_ex* desc);
+int conv_fwd_ex(const convfwd_desc_ex* desc, const void* x, const void* w, void* y, void* stream);
+int conv_fwd_path_ex(const convfwd_desc_ex* desc, int path, const void* x, const void* w, void* y,
+                     void* stream);
 
 /* Static message for a return code; never NULL. */
 const char* conv_strerror(int code);

@@ -68,7 +68,8 @@ def test_out_shape_table_from_pages():
     ("d", 0, -2), ("h", -1, -2), ("c_in", 0, -2), ("c_out", 0, -2), ("k_w", 0, -2),
     ("s_h", 0, -2), ("p_d", -1, -2), ("n", -1, -2),
     ("k_h", 12, -2),            # 5 + 2 < 12: empty output
-    ("groups", 2, -3), ("dtype", 7, -3),
+    ("groups", 0, -2), ("groups", 3, -2),   # groups must be >= 1 and divide C_in and C_out
+    ("dtype", 7, -3),
 ])
 def test_validation_codes(field, value, code):
     rc, _ = _out_shape(_desc(**{field: value}))
@@ -163,3 +164,76 @@ def test_binding_refuses_cpu_tensors():
     w = torch.zeros(4, 3, 3, 4, dtype=torch.float16)
     with pytest.raises(ValueError):
         igc.conv_fwd(x, w, 1, 1)
+
+
+
+# ---- the extended descriptor: low / high pads, dilation, groups ---------------------------
+
+def _desc_ex(**kw):
+    base = dict(n=2, d=4, h=5, w=6, c_in=8, c_out=4, k_d=3, k_h=3, k_w=3, s_d=1, s_h=1, s_w=1,
+                p_d=1, p_h=1, p_w=1, q_d=1, q_h=1, q_w=1, e_d=1, e_h=1, e_w=1, groups=1, dtype=1)
+    base.update(kw)
+    return igc.DescEx(**base)
+
+
+def _out_shape_ex(d):
+    out = (ctypes.c_int64 * 5)()
+    rc = igc.lib().conv_out_shape_ex(ctypes.byref(d), out)
+    return rc, tuple(out)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("e_d", 0, -2), ("e_w", -1, -2), ("q_h", -1, -2), ("groups", 0, -2), ("groups", 3, -2),
+    ("e_h", 4, -2),             # 5 + 2 < 4*(3-1)+1: empty output
+    ("dtype", 9, -3),
+])
+def test_validation_codes_ex(field, value, code):
+    rc, _ = _out_shape_ex(_desc_ex(**{field: value}))
+    assert rc == code
+    assert igc.lib().conv_fwd_ex(ctypes.byref(_desc_ex(**{field: value})), 16, 4096, 1 << 20, None) == code
+
+
+@pytest.mark.parametrize("dims,pads,dil", [
+    ((4, 5, 6), ((1, 0), (0, 2), (2, 1)), (1, 2, 1)),
+    ((7, 9, 8), ((0, 0), (1, 1), (3, 0)), (2, 1, 3)),
+    ((1, 11, 13), ((0, 0), (2, 3), (1, 4)), (1, 3, 2)),
+])
+def test_out_shape_ex_matches_oracle(dims, pads, dil):
+    x_shape, w_shape, st = (2, *dims, 6), (4, 1 if dims[0] == 1 else 3, 3, 3, 3), (1, 2, 2)
+    got = igc.out_shape(x_shape, w_shape, st, pads, dil, groups=2)
+    expect = (2, *[oracle.out_extent_ex(dims[i], w_shape[1 + i], st[i], pads[i][0], pads[i][1], dil[i])
+                   for i in range(3)], 4)
+    assert got == expect
+
+
+def test_plain_descriptor_equals_extended_with_symmetric_pads():
+    """conv_out_shape / conv_select_path of a convfwd_desc agree with the extended calls
+    for q = p and e = 1, for every workload shape."""
+    for wl in WORKLOADS.values():
+        assert igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding) == \
+            igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, [(q, q) for q in wl.padding], 1, 1)
+        d = igc.make_desc(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.torch_dtype)
+        assert igc.lib().conv_select_path(ctypes.byref(d)) == \
+            igc.lib().conv_select_path_ex(ctypes.byref(igc.make_desc_ex(
+                wl.x_shape, wl.w_shape, wl.stride, wl.padding, 1, 1, wl.torch_dtype)))
+
+
+@pytest.mark.parametrize("path,ok", [(1, True), (7, True), (4, True), (2, False), (3, False), (5, False), (6, False)])
+def test_grouped_problem_path_acceptance(path, ok):
+    """Grouped problems (here C_in/G = 64): main, runs and direct take them; flat-K, rows, brick
+    and strip do not (the last returns UNSUPPORTED instead of computing something else)."""
+    d = _desc_ex(n=0, c_in=128, c_out=64, groups=2, w=32, p_w=1, q_w=1)
+    assert igc.lib().conv_fwd_path_ex(ctypes.byref(d), path, None, None, None, None) == (0 if ok else -3)
+
+
+@pytest.mark.parametrize("path,ok", [(1, True), (7, True), (4, True), (6, False), (2, False)])
+def test_w_dilated_problem_path_acceptance(path, ok):
+    d = _desc_ex(n=0, c_in=64, c_out=64, w=40, e_w=2, p_w=2, q_w=2)
+    assert igc.lib().conv_fwd_path_ex(ctypes.byref(d), path, None, None, None, None) == (0 if ok else -3)
+
+
+def test_auto_path_for_variants():
+    assert igc.select_path((2, 8, 8, 8, 128), (64, 3, 3, 3, 64), 1, 1, torch.float16, groups=2) == "main"
+    assert igc.select_path((2, 8, 8, 8, 32), (32, 3, 3, 3, 1), 1, 1, torch.float16, groups=32) == "runs"
+    assert igc.select_path((2, 16, 16, 64), (64, 3, 3, 64), 1, 2, torch.float16, dilation=2) == "main"
+    assert igc.select_path((2, 8, 8, 32, 64), (64, 3, 3, 3, 64), 1, 1, torch.float16, dilation=(2, 2, 1)) == "strip"

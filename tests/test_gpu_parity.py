@@ -234,3 +234,101 @@ def test_wrong_out_rejected():
         igc.conv_fwd(x, w, 1, 1, out=torch.empty((1, 4, 4, 4, 63), dtype=torch.float16, device=DEV))
     with pytest.raises(igc.ConvError):
         igc.conv_fwd(x, w, 1, 1, path="rows")
+
+
+# ---- the variants: grouped, dilated, padded differently per side -------------------------
+
+VARIANTS = [
+    # name, dtype, x shape, w shape (C_in/G last), stride, (low, high) pads, dilation, groups
+    ("grouped3d_bf16_g2_c64", "bf16", (2, 6, 7, 9, 128), (64, 3, 3, 3, 64), (1, 1, 1),
+     ((1, 1), (1, 1), (1, 1)), (1, 1, 1), 2),
+    ("resnext2d_fp16_g32_c4", "fp16", (2, 14, 15, 128), (128, 3, 3, 4), (1, 1), ((1, 1), (1, 1)), (1, 1), 32),
+    ("depthwise2d_fp16_c48", "fp16", (2, 16, 17, 48), (48, 3, 3, 1), (1, 1), ((1, 1), (1, 1)), (1, 1), 48),
+    ("dilated2d_fp16_e2", "fp16", (2, 20, 33, 64), (64, 3, 3, 64), (1, 1), ((2, 2), (2, 2)), (2, 2), 1),
+    ("dilated3d_bf16_dh2_w32", "bf16", (1, 7, 9, 32, 64), (64, 3, 3, 3, 64), (1, 1, 1),
+     ((2, 2), (2, 2), (1, 1)), (2, 2, 1), 1),
+    ("asympad3d_fp16_w32", "fp16", (2, 5, 6, 32, 64), (128, 3, 3, 3, 64), (1, 1, 1),
+     ((0, 2), (1, 0), (0, 2)), (1, 1, 1), 1),
+    ("grouped_dilated_fp32", "fp32", (1, 5, 6, 7, 12), (6, 3, 2, 3, 4), (1, 1, 1),
+     ((1, 1), (2, 0), (1, 2)), (1, 2, 2), 3),
+    ("all_variants_bf16_g2", "bf16", (2, 9, 10, 11, 128), (64, 3, 3, 3, 64), (2, 1, 2),
+     ((2, 1), (0, 1), (3, 2)), (2, 1, 2), 2),
+    ("grouped_odd_channels_bf16", "bf16", (2, 5, 6, 7, 45), (30, 3, 3, 3, 15), (1, 1, 1),
+     ((1, 1), (1, 1), (1, 1)), (1, 1, 1), 3),
+]
+VARIANT_PATHS = ["main", "strip", "runs", "direct"]
+
+
+def _v_accepts(v, path):
+    name, dtype, xs, ws, st, pads, dil, g = v
+    half = dtype in ("fp16", "bf16")
+    cin_g, cout_g = xs[-1] // g, ws[0] // g
+    if path == "main":
+        return half and cin_g % 32 == 0 and cout_g % 4 == 0
+    if path == "strip":
+        ow = (xs[-2] + pads[-1][0] + pads[-1][1] - dil[-1] * (ws[-2] - 1) - 1) // st[-1] + 1
+        return (half and g == 1 and dil[-1] == 1 and xs[-1] % 32 == 0 and ws[0] % 4 == 0
+                and st[-1] == 1 and ow % 32 == 0 and ws[-2] <= 5)
+    return True
+
+
+def _v_inputs(v):
+    name, dtype, xs, ws, st, pads, dil, g = v
+    gen = torch.Generator("cpu").manual_seed(hash(name) % (2 ** 31))
+    x = (torch.rand(xs, generator=gen) * 2 - 1).to(_dt(dtype))
+    fan_in = int(np.prod(ws[1:]))
+    w = (torch.randn(ws, generator=gen) / np.sqrt(fan_in)).to(_dt(dtype))
+    return x.to(DEV), w.to(DEV)
+
+
+@pytest.mark.parametrize("path", VARIANT_PATHS)
+@pytest.mark.parametrize("v", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_parity_variants(v, path):
+    if not _v_accepts(v, path):
+        pytest.skip(f"{path} does not take {v[0]}")
+    name, dtype, xs, ws, st, pads, dil, g = v
+    print(f"[parity] {name} path={path}", flush=True)
+    x, w = _v_inputs(v)
+    y = igc.conv_fwd(x, w, st, pads, path=path, dilation=dil, groups=g)
+    torch.cuda.synchronize()
+    ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), st, pads, dilation=dil, groups=g)
+    assert_parity(oracle.to_float64(y), ref, dtype, f"{name}/{path}")
+
+
+@pytest.mark.parametrize("v", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_variant_tap_count_bit_exact(v):
+    """x = 1, w = 1 on the first channel of each group: every output counts its in-bounds
+    dilated taps; bit-exact on every path that takes the problem."""
+    name, dtype, xs, ws, st, pads, dil, g = v
+    x = torch.ones(xs, dtype=_dt(dtype), device=DEV)
+    w = torch.zeros(ws, dtype=_dt(dtype), device=DEV)
+    w[..., 0] = 1
+    ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), st, pads, dilation=dil, groups=g)
+    for path in VARIANT_PATHS:
+        if _v_accepts(v, path):
+            y = igc.conv_fwd(x, w, st, pads, path=path, dilation=dil, groups=g)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(oracle.to_float64(y), ref, err_msg=f"{name}/{path}")
+
+
+@pytest.mark.parametrize("v", [v for v in VARIANTS if v[2][-1] // v[7] == v[3][0] // v[7]],
+                         ids=[v[0] for v in VARIANTS if v[2][-1] // v[7] == v[3][0] // v[7]])
+def test_variant_one_hot_gather_bit_exact(v):
+    """Per group, w = identity on the group's channels at one tap: y is the shifted, strided,
+    dilated copy of x with channels kept in their group; bit-exact."""
+    name, dtype, xs, ws, st, pads, dil, g = v
+    cg = xs[-1] // g
+    gen = torch.Generator("cpu").manual_seed(5)
+    x = (torch.rand(xs, generator=gen) * 2 - 1).to(_dt(dtype)).to(DEV)
+    ks = ws[1:-1]
+    tap = tuple(k - 1 for k in ks)
+    w = torch.zeros(ws, dtype=_dt(dtype))
+    co = torch.arange(ws[0])
+    w[(co, *[torch.full((ws[0],), t) for t in tap], co % cg)] = 1
+    w = w.to(DEV)
+    ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), st, pads, dilation=dil, groups=g)
+    for path in VARIANT_PATHS:
+        if _v_accepts(v, path):
+            y = igc.conv_fwd(x, w, st, pads, path=path, dilation=dil, groups=g)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(oracle.to_float64(y), ref, err_msg=f"{name}/{path}")
