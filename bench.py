@@ -38,7 +38,7 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 import implicit_gemm_conv_amd as igc  # noqa: E402
-from conv_workloads import HEADLINE, WORKLOADS, make_inputs  # noqa: E402
+from conv_workloads import HEADLINE, VARIANT_WORKLOADS, WORKLOADS, make_inputs  # noqa: E402
 
 PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}   # MI355X dense, published
 METRIC = "conv fwd TFLOP/s (2·M·N·K) and % of MFMA peak, fp16 NDHWC 3×3×3 shapes"
@@ -91,8 +91,15 @@ def copy_calibration(mib=512, reps=5):
                                            "copies": reps}}), flush=True)
 
 
+def _var(wl):
+    """dilation / groups of a workload (1 for the plain ones)."""
+    return dict(dilation=wl.dilation or 1, groups=wl.groups)
+
+
 def gemm_dims(wl):
-    out = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding)
+    """M output positions, N = C_out, K = taps * C_in / groups: 2*M*N*K is the multiply-add
+    count of the sum (grouped layers multiply each output by one group's channels only)."""
+    out = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding, **_var(wl))
     m = int(np.prod(out[:-1]))
     n = wl.w_shape[0]
     k = int(np.prod(wl.w_shape[1:]))
@@ -101,7 +108,7 @@ def gemm_dims(wl):
 
 def kernel_key(wl):
     """The path AUTO takes; on these shapes a path launches one kernel instantiation."""
-    return igc.select_path(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.torch_dtype)
+    return igc.select_path(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.torch_dtype, **_var(wl))
 
 
 def cpu_baseline(wls, inputs, fraction):
@@ -132,11 +139,11 @@ def sweep(launches, names=None):
     """Per-workload event timing, warm (resident buffers) and cold (rotated buffer sets)."""
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
-    for name, wl in WORKLOADS.items():
+    for name, wl in {**WORKLOADS, **VARIANT_WORKLOADS}.items():
         if names and name not in names:
             continue
         x, w = make_inputs(wl, dev)
-        shape = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding)
+        shape = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding, **_var(wl))
         y = torch.empty(shape, dtype=wl.torch_dtype, device=dev)
         m, n, k = gemm_dims(wl)
         flops = 2.0 * m * n * k
@@ -152,7 +159,7 @@ def sweep(launches, names=None):
                    for _ in pairs]
             for (xi, yi), (a, b) in zip(pairs, evs):
                 a.record(stream)
-                igc.conv_fwd(xi, w, wl.stride, wl.padding, out=yi)
+                igc.conv_fwd(xi, w, wl.stride, wl.padding, out=yi, **_var(wl))
                 b.record(stream)
             torch.cuda.synchronize()
             return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])

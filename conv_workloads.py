@@ -37,6 +37,8 @@ class Workload:
     x_dist: str = "uniform"    # "uniform" -> U[-1, 1); "normal" -> N(0, 1)
     seed_x: int = 1
     seed_w: int = 2
+    dilation: tuple = None     # per dimension, None = 1 (the variants only)
+    groups: int = 1            # channel groups (the variants only); w holds C_in/groups channels
 
     @property
     def dims(self) -> int:
@@ -79,6 +81,29 @@ WORKLOADS = {
             (128, 3, 1, 1, 64), (1, 1, 1), (1, 0, 0)),
         _wl(5, 3, "c5d_conv3d_bf16_n4_32c64_o128_k133", "bf16", (4, 32, 32, 32, 64),
             (128, 1, 3, 3, 64), (1, 1, 1), (0, 1, 1)),
+    ]
+}
+
+# The variants the tutorial lists beside the plain convolution ("Convolution
+# variants worth knowing": grouped as in ResNeXt, dilated), plus padding that
+# differs between the two sides of a dimension.  The pages print no shapes for
+# them; these are synthetic layers of the same families at the scale of the
+# plain workloads: a ResNeXt-style grouped 3x3 (32 groups of 4 channels), a
+# dilated 3x3 at 256 channels, a 3D grouped 3x3x3 (2 groups of 64), and a 4x4
+# stride-2 layer padded (1, 2) per side as "same" padding of an even filter
+# needs.  Padding is given as (low, high) per dimension.
+VARIANT_WORKLOADS = {
+    w.name: w for w in [
+        replace(_wl(6, 0, "v1_conv2d_fp16_resnext_n32_56c128_g32", "fp16", (32, 56, 56, 128),
+                    (128, 3, 3, 4), (1, 1), ((1, 1), (1, 1))), groups=32),
+        replace(_wl(6, 1, "v2_conv2d_fp16_dilated2_n8_64c256", "fp16", (8, 64, 64, 256),
+                    (256, 3, 3, 256), (1, 1), ((2, 2), (2, 2))), dilation=(2, 2)),
+        replace(_wl(6, 2, "v3_conv3d_fp16_grouped2_n4_32c128", "fp16", (4, 32, 32, 32, 128),
+                    (128, 3, 3, 3, 64), (1, 1, 1), ((1, 1), (1, 1), (1, 1))), groups=2),
+        _wl(6, 3, "v4_conv2d_fp16_k4s2_asympad_n32_56c64_o128", "fp16", (32, 56, 56, 64),
+            (128, 4, 4, 64), (2, 2), ((1, 2), (1, 2))),
+        replace(_wl(6, 4, "v5_conv3d_fp16_depthwise_n4_32c128", "fp16", (4, 32, 32, 32, 128),
+                    (128, 3, 3, 3, 1), (1, 1, 1), ((1, 1), (1, 1), (1, 1))), groups=128),
     ]
 }
 

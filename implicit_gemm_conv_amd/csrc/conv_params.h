@@ -47,6 +47,8 @@ hipError_t launch_strip(const ConvParams& p, int dtype, const void* x, const voi
                         hipStream_t s);
 hipError_t launch_runs(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
                        hipStream_t s);
+hipError_t launch_grouped(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                          hipStream_t s);
 
 // Whether a path accepts a problem (host-side rules mirrored in convfwd.h).
 bool main_accepts(const ConvParams& p, int dtype);
@@ -55,5 +57,6 @@ bool rows_accepts(const ConvParams& p, int dtype);
 bool brick_accepts(const ConvParams& p, int dtype);
 bool strip_accepts(const ConvParams& p, int dtype);
 bool runs_accepts(const ConvParams& p, int dtype);
+bool grouped_accepts(const ConvParams& p, int dtype);
 
 }  // namespace convfwd

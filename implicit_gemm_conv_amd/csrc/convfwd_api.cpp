@@ -109,6 +109,8 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
 int auto_path(const ConvParams& p, int dtype) {
   // The strip path wins once the w-taps share a strip (K_w >= 2); with K_w = 1
   // it is the main path with a larger tile and the main path is faster.
+  // Few channels per group (down to depthwise): the memory-bound direct form.
+  if (convfwd::grouped_accepts(p, dtype)) return CONVFWD_PATH_GROUPED;
   if (p.kw >= 2 && convfwd::strip_accepts(p, dtype)) return CONVFWD_PATH_STRIP;
   if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;
@@ -125,6 +127,7 @@ bool path_accepts(int path, const ConvParams& p, int dtype) {
     case CONVFWD_PATH_BRICK: return convfwd::brick_accepts(p, dtype);
     case CONVFWD_PATH_STRIP: return convfwd::strip_accepts(p, dtype);
     case CONVFWD_PATH_RUNS: return convfwd::runs_accepts(p, dtype);
+    case CONVFWD_PATH_GROUPED: return convfwd::grouped_accepts(p, dtype);
     default: return false;
   }
 }
@@ -148,6 +151,7 @@ int run(const convfwd_desc_ex* desc, int path, const void* x, const void* w, voi
     case CONVFWD_PATH_BRICK: e = convfwd::launch_brick(p, desc->dtype, x, w, y, s); break;
     case CONVFWD_PATH_STRIP: e = convfwd::launch_strip(p, desc->dtype, x, w, y, s); break;
     case CONVFWD_PATH_RUNS: e = convfwd::launch_runs(p, desc->dtype, x, w, y, s); break;
+    case CONVFWD_PATH_GROUPED: e = convfwd::launch_grouped(p, desc->dtype, x, w, y, s); break;
     default: e = convfwd::launch_direct(p, desc->dtype, x, w, y, s); break;
   }
   if (e != hipSuccess) return CONVFWD_ERR_LAUNCH;
@@ -182,7 +186,7 @@ int conv_fwd_ex(const convfwd_desc_ex* desc, const void* x, const void* w, void*
 
 int conv_fwd_path_ex(const convfwd_desc_ex* desc, int path, const void* x, const void* w, void* y,
                      void* stream) {
-  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_RUNS) return CONVFWD_ERR_UNSUPPORTED;
+  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_GROUPED) return CONVFWD_ERR_UNSUPPORTED;
   return run(desc, path, x, w, y, stream);
 }
 
@@ -234,6 +238,7 @@ const char* conv_path_name(int path) {
     case CONVFWD_PATH_BRICK: return "brick";
     case CONVFWD_PATH_STRIP: return "strip";
     case CONVFWD_PATH_RUNS: return "runs";
+    case CONVFWD_PATH_GROUPED: return "grouped";
     default: return "unknown";
   }
 }

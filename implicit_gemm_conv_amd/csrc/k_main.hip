@@ -285,7 +285,7 @@ hipError_t launch_cfg(const ConvParams& p, const void* x, const void* w, void* y
 // of them for every problem, for tile-size sweeps; by default the choice below
 // depends on the problem size and channel alignment.
 constexpr int variant_bk(int v) {
-  return (v == 1 || v == 4 || v == 7 || v == 9 || v == 10 || v == 12 || v == 13 || v == 41 || v == 43 ||
+  return (v == 1 || v == 4 || v == 7 || v == 9 || v == 10 || v == 12 || v == 13 || v == 14 || v == 41 || v == 43 ||
           v == 45 || v == 47)
              ? 64
              : 32;
@@ -306,6 +306,7 @@ hipError_t launch_variant(int v, const ConvParams& p, const void* x, const void*
     case 11: return launch_cfg<T, 64, 64, 32, 2, 2, 4, 3, 16>(p, x, w, y, s);
     case 12: return launch_cfg<T, 32, 128, 64, 1, 4, 4, 2, 16>(p, x, w, y, s);
     case 13: return launch_cfg<T, 64, 64, 64, 2, 2, 3, 3, 16>(p, x, w, y, s);
+    case 14: return launch_cfg<T, 128, 64, 64, 2, 2, 3, 2, 16>(p, x, w, y, s);
     // 32x32x16 MFMA blocks
     case 41: return launch_cfg<T, 256, 128, 64, 4, 1, 2, 1, 32>(p, x, w, y, s);
     case 42: return launch_cfg<T, 256, 128, 32, 4, 1, 2, 2, 32>(p, x, w, y, s);
@@ -328,6 +329,9 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
 #endif
   const bool bk64 = p.cin_g % 64 == 0;
   const long tiles_256 = (long)((p.M + 255) / 256) * p.groups * ((p.cout_g + 127) / 128);
+  // groups of at most 64 output channels: a 64-wide column tile (a 128-wide one
+  // would leave half its columns idle)
+  if (p.cout_g <= 64 && bk64 && tiles_256 >= 256) return launch_variant<T>(14, p, x, w, y, s);
   if (tiles_256 >= 256) return launch_variant<T>(bk64 ? 4 : 3, p, x, w, y, s);
   return launch_variant<T>(bk64 ? 9 : 8, p, x, w, y, s);
 }

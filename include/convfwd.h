@@ -92,9 +92,12 @@ typedef enum {
                               W_out % 32 == 0, K_w <= 5, K_d, K_h <= 16: per (channel chunk,
                               kd, kh) one input strip per 32-output w-segment staged in LDS,
                               all K_w taps read from it, 512 x 128 tiles, MFMA */
-  CONVFWD_PATH_RUNS = 7    /* any dtype and C_in, filter <= 16 per dim (the unaligned-channel
+  CONVFWD_PATH_RUNS = 7,   /* any dtype and C_in, filter <= 16 per dim (the unaligned-channel
                               tail path and fp32): the K_w * C_in columns of each (kd, kh) read
                               as one contiguous run, 16-byte unaligned pieces, MFMA */
+  CONVFWD_PATH_GROUPED = 8 /* any dtype, G > 1 with C_in/G in {1, 2, 4, 8, 16}, C_out/G <= 16 and
+                              C_out * K_d*K_h*K_w * C_in/G <= 16384 (depthwise and small groups):
+                              one thread per (output position, group), fp32 FMA, filter in LDS */
 } convfwd_path;
 
 /* Problem descriptor.  All extents in elements. */
@@ -155,7 +158,8 @@ int conv_fwd_path_ex(const convfwd_desc_ex* desc, int path, const void* x, const
 /* Static message for a return code; never NULL. */
 const char* conv_strerror(int code);
 
-/* Static name of a path ("auto", "main", "flatk", "rows", "direct", "brick", "strip", "runs");
+/* Static name of a path ("auto", "main", "flatk", "rows", "direct", "brick", "strip", "runs",
+ * "grouped");
  * never NULL. */
 const char* conv_path_name(int path);
 

@@ -134,8 +134,9 @@ def test_strerror_and_path_names():
     lib = igc.lib()
     for code in range(-7, 1):
         assert lib.conv_strerror(code)
-    assert [lib.conv_path_name(i).decode() for i in range(8)] == ["auto", "main", "flatk", "rows",
-                                                                  "direct", "brick", "strip", "runs"]
+    assert [lib.conv_path_name(i).decode() for i in range(9)] == ["auto", "main", "flatk", "rows",
+                                                                  "direct", "brick", "strip", "runs",
+                                                                  "grouped"]
 
 
 EXPECTED_PATHS = {
@@ -234,6 +235,7 @@ def test_w_dilated_problem_path_acceptance(path, ok):
 
 def test_auto_path_for_variants():
     assert igc.select_path((2, 8, 8, 8, 128), (64, 3, 3, 3, 64), 1, 1, torch.float16, groups=2) == "main"
-    assert igc.select_path((2, 8, 8, 8, 32), (32, 3, 3, 3, 1), 1, 1, torch.float16, groups=32) == "runs"
+    assert igc.select_path((2, 8, 8, 8, 32), (32, 3, 3, 3, 1), 1, 1, torch.float16, groups=32) == "grouped"
+    assert igc.select_path((2, 8, 8, 8, 96), (96, 3, 3, 3, 3), 1, 1, torch.float16, groups=32) == "runs"
     assert igc.select_path((2, 16, 16, 64), (64, 3, 3, 64), 1, 2, torch.float16, dilation=2) == "main"
     assert igc.select_path((2, 8, 8, 32, 64), (64, 3, 3, 3, 64), 1, 1, torch.float16, dilation=(2, 2, 1)) == "strip"

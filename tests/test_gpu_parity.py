@@ -14,7 +14,7 @@ import torch
 
 import implicit_gemm_conv_amd as igc
 import oracle
-from conv_workloads import WORKLOADS, Workload, make_inputs
+from conv_workloads import VARIANT_WORKLOADS, WORKLOADS, Workload, make_inputs
 from tests.parity import assert_parity
 
 pytestmark = pytest.mark.gpu
@@ -255,8 +255,26 @@ VARIANTS = [
      ((2, 1), (0, 1), (3, 2)), (2, 1, 2), 2),
     ("grouped_odd_channels_bf16", "bf16", (2, 5, 6, 7, 45), (30, 3, 3, 3, 15), (1, 1, 1),
      ((1, 1), (1, 1), (1, 1)), (1, 1, 1), 3),
+    ("depthwise3d_bf16_mult2_s2", "bf16", (2, 7, 9, 11, 24), (48, 3, 3, 3, 1), (2, 2, 2),
+     ((1, 1), (1, 1), (1, 1)), (1, 1, 1), 24),
+    ("grouped2d_fp32_cg8_og16_dh2", "fp32", (2, 10, 13, 64), (128, 3, 3, 8), (1, 1),
+     ((2, 2), (1, 1)), (2, 1), 8),
+    ("grouped2d_fp16_cg16_og8_k5_s2", "fp16", (1, 12, 19, 64), (32, 5, 5, 16), (1, 2),
+     ((2, 2), (2, 1)), (1, 1), 4),
+    ("grouped2d_bf16_cg2_og3", "bf16", (2, 9, 10, 12), (18, 3, 3, 2), (1, 1),
+     ((0, 1), (1, 1)), (1, 1), 6),
+    ("depthwise2d_fp32_k5_s2_tail", "fp32", (2, 13, 23, 20), (20, 5, 5, 1), (2, 2),
+     ((2, 2), (2, 2)), (1, 1), 20),
+    ("depthwise3d_bf16_k7_tail", "bf16", (1, 5, 9, 19, 16), (16, 3, 3, 7, 1), (1, 1, 1),
+     ((1, 1), (1, 1), (3, 3)), (1, 1, 1), 16),
+    ("grouped2d_fp16_cg8_k7_s2", "fp16", (2, 9, 30, 32), (32, 7, 7, 8), (1, 2),
+     ((3, 3), (3, 3)), (1, 1), 4),
+    ("grouped2d_bf16_cg2_k1", "bf16", (2, 5, 11, 16), (16, 1, 1, 2), (1, 1),
+     ((0, 0), (0, 0)), (1, 1), 8),
+    ("depthwise3d_fp16_dil_dh_sh2", "fp16", (1, 8, 9, 10, 24), (24, 3, 3, 3, 1), (1, 2, 1),
+     ((2, 2), (2, 1), (1, 1)), (2, 2, 1), 24),
 ]
-VARIANT_PATHS = ["main", "strip", "runs", "direct"]
+VARIANT_PATHS = ["main", "strip", "runs", "grouped", "direct"]
 
 
 def _v_accepts(v, path):
@@ -265,6 +283,9 @@ def _v_accepts(v, path):
     cin_g, cout_g = xs[-1] // g, ws[0] // g
     if path == "main":
         return half and cin_g % 32 == 0 and cout_g % 4 == 0
+    if path == "grouped":
+        return (g > 1 and cin_g in (1, 2, 4, 8, 16) and cout_g <= 16
+                and ws[0] * int(np.prod(ws[1:])) <= 16384)
     if path == "strip":
         ow = (xs[-2] + pads[-1][0] + pads[-1][1] - dil[-1] * (ws[-2] - 1) - 1) // st[-1] + 1
         return (half and g == 1 and dil[-1] == 1 and xs[-1] % 32 == 0 and ws[0] % 4 == 0
@@ -332,3 +353,23 @@ def test_variant_one_hot_gather_bit_exact(v):
             y = igc.conv_fwd(x, w, st, pads, path=path, dilation=dil, groups=g)
             torch.cuda.synchronize()
             np.testing.assert_array_equal(oracle.to_float64(y), ref, err_msg=f"{name}/{path}")
+
+
+
+@pytest.mark.parametrize("name", sorted(VARIANT_WORKLOADS))
+def test_parity_variant_workloads_full_size_sampled(name):
+    """The variant workloads at full size on the auto path (as bench.py --sweep runs them),
+    checked on sampled output rows."""
+    wl = VARIANT_WORKLOADS[name]
+    kw = dict(dilation=wl.dilation or 1, groups=wl.groups)
+    print(f"[full] {name} path={igc.select_path(wl.x_shape, wl.w_shape, wl.stride, wl.padding, wl.torch_dtype, **kw)}",
+          flush=True)
+    x, w = make_inputs(wl, DEV)
+    y = igc.conv_fwd(x, w, wl.stride, wl.padding, **kw)
+    torch.cuda.synchronize()
+    yf = y.reshape(-1, y.shape[-1])
+    rows = _sample_rows(yf.shape[0], 2048, seed=wl.seed_x)
+    ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), wl.stride, wl.padding, rows=rows, **kw)
+    got = oracle.to_float64(yf[torch.from_numpy(rows).to(DEV)])
+    assert_parity(got, ref, wl.dtype, name)
+    assert torch.isfinite(y.float()).all()
