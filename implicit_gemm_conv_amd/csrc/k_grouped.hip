@@ -9,16 +9,21 @@
 //
 // Two kernels.  The tiled one takes groups with as many output as input
 // channels (C_out/G == C_in/G, depthwise included) when 16 bytes of channels
-// hold whole groups, filters up to 7 wide, stride 1 or 2 and no dilation
+// hold whole groups, filters 1, 3, 5 or 7 wide, stride 1 or 2 and no dilation
 // along w.  A thread owns one 16-byte slice of channels (8 fp16/bf16 or 4
 // fp32, whole groups, so the slice's outputs need only the slice's inputs) and
 // a run of TW consecutive outputs along w.  For each (kd, kh) it loads the
 // (TW-1)*s + K_w input positions its outputs' windows cover, each one 16-byte
 // load, all in flight together, and reuses every load across the K_w taps that
-// read it.  The filter is staged once per workgroup in LDS as fp32, reordered
-// to (tap, C_out, C_in/G) so that one tap's weights for a slice are adjacent.
-// Consecutive threads take consecutive slices of one output position, so a
-// wave's loads and stores cover whole rows of channels.
+// read it.  Groups of two or more 16-bit channels use two-channel dot products
+// with fp32 accumulation (v_dot2_f32_f16 / v_dot2_f32_bf16), halving the
+// instruction count; depthwise layers use one fp32 FMA per product (fp16
+// operands feed v_fma_mix_f32 directly).  The filter is staged once per
+// workgroup in LDS, reordered to (tap, C_out, C_in/G) so that one tap's weights
+// for a slice are adjacent.  The grid is persistent, sized to what the chip
+// holds at four waves per SIMD.  Consecutive threads take consecutive slices of
+// one output position, so a wave's loads and stores cover whole rows of
+// channels.
 //
 // The general kernel takes everything else the path accepts (other channel
 // ratios, dilation along w, odd channel counts, unaligned tensors): one
@@ -54,96 +59,151 @@ template <> __device__ __forceinline__ float slice_elem<__bf16>(const u4& v, int
   return __builtin_bit_cast(float, (j & 1) ? (d & 0xffff0000u) : (d << 16));
 }
 
+// Outputs along w per thread of the tiled kernel: as many as fit in the
+// register budget of four waves per SIMD (accumulators, the window row's
+// loads and one tap's weights).
+template <int CG, int KW, int SW>
+constexpr int tiled_tw() {
+  return (CG <= 2 && KW * SW <= 3) ? 8 : (CG <= 4 ? 4 : 2);
+}
+
+// Dot products of pairs of channels (v_dot2_f32_{f16,bf16}: two products
+// and an fp32 accumulate in one instruction) for 16-bit groups of two or more
+// channels; fp32 FMAs otherwise.
+template <typename T> struct Pair;
+template <> struct Pair<_Float16> { typedef _Float16 type __attribute__((ext_vector_type(2))); };
+template <> struct Pair<__bf16> { typedef __bf16 type __attribute__((ext_vector_type(2))); };
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, _Float16*) {
+  typedef Pair<_Float16>::type P;
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(P, a), __builtin_bit_cast(P, b), c, false);
+}
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c, __bf16*) {
+  typedef Pair<__bf16>::type P;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(P, a), __builtin_bit_cast(P, b), c, false);
+}
+
+template <typename T, int CG>
+constexpr bool use_dot2() { return sizeof(T) == 2 && CG >= 2; }
+
 // ---- tiled kernel: C_out/G == C_in/G = CG, 16-byte slices, K_w = KW, stride SW ----
+// Persistent: the grid is at most what the chip holds at four waves per
+// SIMD, and each thread strides over (slice, run of TW outputs) units.
 template <typename T, int CG, int KW, int SW>
-__global__ __launch_bounds__(256) void conv_grouped_tiled_kernel(ConvParams p, const T* __restrict__ x,
-                                                                 const T* __restrict__ w,
-                                                                 T* __restrict__ y, int tiles_w) {
+__global__ __launch_bounds__(256, 4) void conv_grouped_tiled_kernel(ConvParams p, const T* __restrict__ x,
+                                                                    const T* __restrict__ w,
+                                                                    T* __restrict__ y, int tiles_w) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int VE = 16 / (int)sizeof(T);      // channels per slice
-  constexpr int TW = CG >= 8 ? 4 : 8;          // outputs along w per thread
+  constexpr int TW = tiled_tw<CG, KW, SW>();   // outputs along w per unit
   constexpr int NP = (TW - 1) * SW + KW;       // input positions per window row
-  constexpr int NW = VE * CG;                  // one tap's weights for a slice
-  extern __shared__ float wls[];               // [tap][C_out][CG], fp32
+  constexpr bool D2 = use_dot2<T, CG>();
+  // one tap's weights for a slice: VE * CG values, as fp32 or as channel pairs
+  constexpr int NWD = D2 ? VE * CG / 2 : VE * CG;
+  extern __shared__ uint32_t wls[];            // [tap][C_out][CG]: fp32, or T pairs
 
-  const int ntaps = p.kd * p.kh * KW;
-  const int wtotal = p.cout * p.K;
-  for (int i = threadIdx.x; i < wtotal; i += 256) {
-    const int c = i % CG, r = i / CG;
-    const int tap = r % ntaps, co = r / ntaps;
-    wls[(tap * p.cout + co) * CG + c] = to_f32(w[i]);
+  // Filter element i = co * K + k (k = tap * CG + c) moves to (tap, co, c).
+  // The workgroup reads consecutive elements; each thread steps (co, k) by
+  // 256 elements incrementally instead of dividing by K per element.
+  {
+    const int wtotal = p.cout * p.K;
+    const int dq = 256 / p.K, dr = 256 % p.K;
+    int co = threadIdx.x / p.K, k = threadIdx.x % p.K;
+    for (int i = threadIdx.x; i < wtotal; i += 256) {
+      const int dst = ((k / CG) * p.cout + co) * CG + (k % CG);   // CG is a power of two
+      if constexpr (D2) ((T*)wls)[dst] = w[i];
+      else ((float*)wls)[dst] = to_f32(w[i]);
+      co += dq;
+      k += dr;
+      if (k >= p.K) { k -= p.K; ++co; }
+    }
   }
   __syncthreads();
 
+  // Unit counts stay below 2^31: x and y are below 2^31 bytes.
   const int U = p.cin / VE;                    // slices per position
-  const int64_t units = (int64_t)p.n * p.od * p.oh * tiles_w * U;
-  const int64_t idx = (int64_t)xcd_tile(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
-  if (idx >= units) return;
-  const int u = (int)(idx % U);
-  int64_t r = idx / U;
-  const int twi = (int)(r % tiles_w);
-  r /= tiles_w;
-  const int yo = (int)(r % p.oh);
-  r /= p.oh;
-  const int zo = (int)(r % p.od);
-  const int n = (int)(r / p.od);
-  const int ow0 = twi * TW;
-  const int xi0 = ow0 * SW - p.pw;
-
+  const int units = p.n * p.od * p.oh * tiles_w * U;
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)x, (short)0, (int)((int64_t)p.n * p.xs_n * (int)sizeof(T)), kRawBufferFlags);
 
-  float acc[TW][VE];
-#pragma unroll
-  for (int t = 0; t < TW; ++t)
-#pragma unroll
-    for (int j = 0; j < VE; ++j) acc[t][j] = 0.f;
+  for (int idx = blockIdx.x * 256 + threadIdx.x; idx < units; idx += gridDim.x * 256) {
+    const int u = idx % U;
+    int r = idx / U;
+    const int twi = r % tiles_w;
+    r /= tiles_w;
+    const int yo = r % p.oh;
+    r /= p.oh;
+    const int zo = r % p.od;
+    const int n = r / p.od;
+    const int ow0 = twi * TW;
+    const int xi0 = ow0 * SW - p.pw;
 
-  for (int a = 0; a < p.kd; ++a) {
-    const int zi = zo * p.sd - p.pd + a * p.ed;
-    if (zi < 0 || zi >= p.d) continue;
-    for (int b = 0; b < p.kh; ++b) {
-      const int yi = yo * p.sh - p.ph + b * p.eh;
-      if (yi < 0 || yi >= p.h) continue;
-      const int row = n * p.xs_n + zi * p.xs_d + yi * p.xs_h + u * VE;
-      u4 xv[NP];
+    float acc[TW][VE];
 #pragma unroll
-      for (int j = 0; j < NP; ++j) {
-        const int xi = xi0 + j;
-        const bool ok = xi >= 0 && xi < p.w;
-        xv[j] = __builtin_amdgcn_raw_buffer_load_b128(
-            xr, ok ? (uint32_t)((row + xi * p.xs_w) * (int)sizeof(T)) : kOutOfRange, 0, 0);
-      }
-      const float* wrow = wls + ((a * p.kh + b) * KW * p.cout + u * VE) * CG;
+    for (int t = 0; t < TW; ++t)
 #pragma unroll
-      for (int e = 0; e < KW; ++e) {
-        float wv[NW];
-        const f32x4_t* wp = (const f32x4_t*)(wrow + e * p.cout * CG);
+      for (int j = 0; j < VE; ++j) acc[t][j] = 0.f;
+
+    for (int a = 0; a < p.kd; ++a) {
+      const int zi = zo * p.sd - p.pd + a * p.ed;
+      if (zi < 0 || zi >= p.d) continue;
+      for (int b = 0; b < p.kh; ++b) {
+        const int yi = yo * p.sh - p.ph + b * p.eh;
+        if (yi < 0 || yi >= p.h) continue;
+        const int row = n * p.xs_n + zi * p.xs_d + yi * p.xs_h + u * VE;
+        u4 xv[NP];
 #pragma unroll
-        for (int q = 0; q < NW / 4; ++q) {
-          const f32x4_t v = wp[q];
-          wv[4 * q] = v[0]; wv[4 * q + 1] = v[1]; wv[4 * q + 2] = v[2]; wv[4 * q + 3] = v[3];
+        for (int j = 0; j < NP; ++j) {
+          const int xi = xi0 + j;
+          const bool ok = xi >= 0 && xi < p.w;
+          xv[j] = __builtin_amdgcn_raw_buffer_load_b128(
+              xr, ok ? (uint32_t)((row + xi * p.xs_w) * (int)sizeof(T)) : kOutOfRange, 0, 0);
         }
-        // channel outermost: consecutive FMAs update different accumulators
+        // this slice's weights of tap (a, b, 0), in dwords
+        const uint32_t* wrow = wls + ((a * p.kh + b) * KW * p.cout + u * VE) * CG / (D2 ? 2 : 1);
 #pragma unroll
-        for (int c = 0; c < CG; ++c)
+        for (int e = 0; e < KW; ++e) {
+          uint32_t wv[NWD];
+          const u4* wp = (const u4*)(wrow + e * p.cout * CG / (D2 ? 2 : 1));
 #pragma unroll
-          for (int t = 0; t < TW; ++t)
+          for (int q = 0; q < NWD / 4; ++q) {
+            const u4 v = wp[q];
+            wv[4 * q] = v[0]; wv[4 * q + 1] = v[1]; wv[4 * q + 2] = v[2]; wv[4 * q + 3] = v[3];
+          }
+          if constexpr (D2) {
+            // output o (group o / CG) takes the CG / 2 channel pairs of its group
 #pragma unroll
-            for (int o = 0; o < VE; ++o)   // (o / CG) * CG is the first channel of o's group
-              acc[t][o] = fmaf(slice_elem<T>(xv[t * SW + e], (o / CG) * CG + c), wv[o * CG + c], acc[t][o]);
+            for (int c2 = 0; c2 < CG / 2; ++c2)
+#pragma unroll
+              for (int t = 0; t < TW; ++t)
+#pragma unroll
+                for (int o = 0; o < VE; ++o)
+                  acc[t][o] = dot2(xv[t * SW + e][(o / CG) * (CG / 2) + c2], wv[o * (CG / 2) + c2],
+                                   acc[t][o], (T*)nullptr);
+          } else {
+            // channel outermost: consecutive FMAs update different accumulators
+#pragma unroll
+            for (int c = 0; c < CG; ++c)
+#pragma unroll
+              for (int t = 0; t < TW; ++t)
+#pragma unroll
+                for (int o = 0; o < VE; ++o)   // (o / CG) * CG is the first channel of o's group
+                  acc[t][o] = fmaf(slice_elem<T>(xv[t * SW + e], (o / CG) * CG + c),
+                                   __builtin_bit_cast(float, wv[o * CG + c]), acc[t][o]);
+          }
+        }
       }
     }
-  }
 
-  T* yrow = y + ((((int64_t)n * p.od + zo) * p.oh + yo) * p.ow) * p.cout + u * VE;
+    T* yrow = y + ((((int64_t)n * p.od + zo) * p.oh + yo) * p.ow) * p.cout + u * VE;
 #pragma unroll
-  for (int t = 0; t < TW; ++t) {
-    if (ow0 + t < p.ow) {
-      T out[VE];
+    for (int t = 0; t < TW; ++t) {
+      if (ow0 + t < p.ow) {
+        T out[VE];
 #pragma unroll
-      for (int j = 0; j < VE; ++j) out[j] = from_f32<T>(acc[t][j]);
-      *(u4*)(yrow + (int64_t)(ow0 + t) * p.cout) = __builtin_bit_cast(u4, out);
+        for (int j = 0; j < VE; ++j) out[j] = from_f32<T>(acc[t][j]);
+        *(u4*)(yrow + (int64_t)(ow0 + t) * p.cout) = __builtin_bit_cast(u4, out);
+      }
     }
   }
 #endif
@@ -215,21 +275,40 @@ __global__ __launch_bounds__(256) void conv_grouped_kernel(ConvParams p, const T
   }
 }
 
-template <typename T, int CG, int KW>
-hipError_t launch_tiled_kw(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
+// Workgroups the device holds at once at four waves per SIMD (one 256-thread
+// workgroup per SIMD set of a CU, four per CU), looked up once per device.
+int resident_groups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = 4 * cus;
+  }
+  return cached[dev];
+}
+
+template <typename T, int CG, int KW, int SW>
+hipError_t launch_tiled_sw(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   constexpr int VE = 16 / (int)sizeof(T);
-  constexpr int TW = CG >= 8 ? 4 : 8;
+  constexpr int TW = tiled_tw<CG, KW, SW>();
   const int tiles_w = (p.ow + TW - 1) / TW;
   const int64_t units = (int64_t)p.n * p.od * p.oh * tiles_w * (p.cin / VE);
-  const unsigned blocks = (unsigned)((units + 255) / 256);
-  const size_t lds = (size_t)p.cout * p.K * sizeof(float);
-  if (p.sw == 1)
-    hipLaunchKernelGGL((conv_grouped_tiled_kernel<T, CG, KW, 1>), dim3(blocks), dim3(256), lds, s, p,
-                       (const T*)x, (const T*)w, (T*)y, tiles_w);
-  else
-    hipLaunchKernelGGL((conv_grouped_tiled_kernel<T, CG, KW, 2>), dim3(blocks), dim3(256), lds, s, p,
-                       (const T*)x, (const T*)w, (T*)y, tiles_w);
+  int64_t blocks = (units + 255) / 256;
+  const int cap = resident_groups();
+  if (blocks > cap) blocks = cap;
+  const size_t lds = (size_t)p.cout * p.K * (use_dot2<T, CG>() ? sizeof(T) : sizeof(float));
+  hipLaunchKernelGGL((conv_grouped_tiled_kernel<T, CG, KW, SW>), dim3((unsigned)blocks), dim3(256), lds, s,
+                     p, (const T*)x, (const T*)w, (T*)y, tiles_w);
   return hipGetLastError();
+}
+
+template <typename T, int CG, int KW>
+hipError_t launch_tiled_kw(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
+  if (p.sw == 1) return launch_tiled_sw<T, CG, KW, 1>(p, x, w, y, s);
+  return launch_tiled_sw<T, CG, KW, 2>(p, x, w, y, s);
 }
 
 template <typename T, int CG>
