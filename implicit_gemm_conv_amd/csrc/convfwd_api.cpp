@@ -107,10 +107,10 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
 // The brick path is available on request; on the measured shapes the
 // per-tap-gather main path is faster, so AUTO does not pick it.
 int auto_path(const ConvParams& p, int dtype) {
+  // Few channels per group (down to depthwise): the memory-bound vector-ALU form.
+  if (convfwd::grouped_accepts(p, dtype)) return CONVFWD_PATH_GROUPED;
   // The strip path wins once the w-taps share a strip (K_w >= 2); with K_w = 1
   // it is the main path with a larger tile and the main path is faster.
-  // Few channels per group (down to depthwise): the memory-bound direct form.
-  if (convfwd::grouped_accepts(p, dtype)) return CONVFWD_PATH_GROUPED;
   if (p.kw >= 2 && convfwd::strip_accepts(p, dtype)) return CONVFWD_PATH_STRIP;
   if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;
