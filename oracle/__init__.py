@@ -1,4 +1,4 @@
-"""CPU oracle for the channels-last convolution forward pass -- TEST INFRASTRUCTURE.
+"""CPU oracle for the channels-last convolution forward and backward-data passes -- TEST INFRASTRUCTURE.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -39,6 +39,9 @@ def _load():
         lib.oracle_conv_fwd.restype = ctypes.c_int64
         lib.oracle_conv_fwd.argtypes = [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.oracle_conv_bwd_data.restype = ctypes.c_int64
+        lib.oracle_conv_bwd_data.argtypes = [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p]
         lib.oracle_out_extent.restype = ctypes.c_int64
         lib.oracle_out_extent.argtypes = [ctypes.c_int64] * 4
         lib.oracle_out_extent_ex.restype = ctypes.c_int64
@@ -118,6 +121,39 @@ def conv_fwd(x: np.ndarray, w: np.ndarray, stride=1, padding=0, rows=None,
     if rows is None and dims == 2:
         y = y.reshape(y.shape[0], *y.shape[2:])
     return (y, int(macs)) if return_macs else y
+
+
+def conv_bwd_data(dy: np.ndarray, w: np.ndarray, x_shape, stride=1, padding=0, dilation=1,
+                  groups: int = 1, return_macs: bool = False):
+    """Backward-data of the forward convolution (x_shape, w, stride, padding, dilation, groups),
+    float64: dx with shape x_shape from dy with the forward output's shape.  Arguments as for
+    ``conv_fwd``; the definition is in conv_oracle.c (the adjoint of the forward map)."""
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    w = np.ascontiguousarray(w, dtype=np.float64)
+    x_shape = tuple(int(e) for e in x_shape)
+    dims = len(x_shape) - 2
+    assert dims in (2, 3) and w.ndim == len(x_shape) and dy.ndim == len(x_shape)
+    assert w.shape[-1] * groups == x_shape[-1] and dy.shape[-1] == w.shape[0]
+    st = _triple(stride, dims)
+    dl = _triple(dilation, dims)
+    pp = _pads(padding, dims)
+    if dims == 2:
+        xs5 = (x_shape[0], 1, *x_shape[1:])
+        w5 = w.reshape(w.shape[0], 1, *w.shape[1:])
+        dy5 = dy.reshape(dy.shape[0], 1, *dy.shape[1:])
+        st, dl, pp = (1,) + st, (1,) + dl, ((0, 0),) + pp
+    else:
+        xs5, w5, dy5 = x_shape, w, dy
+    outs = [out_extent_ex(xs5[1 + i], w5.shape[1 + i], st[i], pp[i][0], pp[i][1], dl[i]) for i in range(3)]
+    assert tuple(dy5.shape) == (xs5[0], *outs, w5.shape[0]), (dy5.shape, outs)
+    sh = _Shape(*xs5, w5.shape[0], w5.shape[1], w5.shape[2], w5.shape[3], *st, *(p[0] for p in pp),
+                *(p[1] for p in pp), *dl, groups)
+    dx = np.zeros(xs5, dtype=np.float64)
+    macs = _load().oracle_conv_bwd_data(ctypes.byref(sh), dy5.ctypes.data, w5.ctypes.data, dx.ctypes.data)
+    if macs < 0:
+        raise ValueError("oracle rejected the shape")
+    dx = dx.reshape(x_shape)
+    return (dx, int(macs)) if return_macs else dx
 
 
 def to_float64(t) -> np.ndarray:

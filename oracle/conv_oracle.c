@@ -39,6 +39,22 @@
  * (N, D_out, H_out, W_out, C_out), all dense, C fastest.  A 2D problem is the
  * 3D one with D = KD = sd = 1 and pd = 0.
  *
+ * Backward-data (the gradient with respect to x, "dgrad") is the transposed
+ * convolution of the tutorial's variant list ("Convolution variants worth
+ * knowing": transposed, upsampling convolution): the adjoint of the forward
+ * map.  Every forward product x(n, i, c) * w[co, k, c] that feeds y[n, o, co]
+ * sends dy[n, o, co] * w[co, k, c] back to dx[n, i, c]:
+ *
+ *   dx[n,id,ih,iw,c] = sum over co of c's group, kd, kh, kw such that
+ *        od = (id + pd - kd*ed) / sd is a whole number with 0 <= od < D_out
+ *        (likewise oh, ow) of dy[n,od,oh,ow,co] * w[co,kd,kh,kw,c - g*C_in/G]
+ *
+ * Written out this way it is also what the MLX pull request's general path
+ * ("input dilation", "flip") computes: a forward convolution of dy with s-1
+ * zeros inserted between neighbours, against the spatially flipped filter with
+ * input and output channels exchanged.  dx has x's shape; positions that no
+ * output window covers get 0.
+ *
  * Arithmetic: every value is a double; every product of two fp16, bf16 or
  * fp32 inputs is exact in double, and the sum is accumulated in double in
  * the loop order below.  The loop runs over every tap, padding included,
@@ -138,6 +154,59 @@ int64_t oracle_conv_fwd(const oracle_conv_shape* s, const double* x, const doubl
               macs += 1;
             }
       y[r * s->c_out + co] = acc;
+    }
+  }
+  return macs;
+}
+
+/*
+ * Backward-data: dx (x's shape) from dy (y's shape) and the forward filter w,
+ * for the forward problem *s.  Returns the number of multiply-adds done, or -1
+ * for a malformed shape.
+ */
+int64_t oracle_conv_bwd_data(const oracle_conv_shape* s, const double* dy, const double* wt, double* dx) {
+  if (s->n < 0 || s->d < 1 || s->h < 1 || s->w < 1 || s->c_in < 1 || s->c_out < 1) return -1;
+  if (s->k_d < 1 || s->k_h < 1 || s->k_w < 1) return -1;
+  if (s->s_d < 1 || s->s_h < 1 || s->s_w < 1) return -1;
+  if (s->p_d < 0 || s->p_h < 0 || s->p_w < 0) return -1;
+  if (s->q_d < 0 || s->q_h < 0 || s->q_w < 0) return -1;
+  if (s->e_d < 1 || s->e_h < 1 || s->e_w < 1) return -1;
+  if (s->groups < 1 || s->c_in % s->groups != 0 || s->c_out % s->groups != 0) return -1;
+  const int64_t od_n = oracle_out_extent_ex(s->d, s->k_d, s->s_d, s->p_d, s->q_d, s->e_d);
+  const int64_t oh_n = oracle_out_extent_ex(s->h, s->k_h, s->s_h, s->p_h, s->q_h, s->e_h);
+  const int64_t ow_n = oracle_out_extent_ex(s->w, s->k_w, s->s_w, s->p_w, s->q_w, s->e_w);
+  if (od_n < 1 || oh_n < 1 || ow_n < 1) return -1;
+  const int64_t cg = s->c_in / s->groups;
+  const int64_t og = s->c_out / s->groups;
+  const int64_t positions = s->n * s->d * s->h * s->w;
+  int64_t macs = 0;
+
+#pragma omp parallel for schedule(dynamic, 16) reduction(+ : macs)
+  for (int64_t r = 0; r < positions; ++r) {
+    const int64_t iw = r % s->w;
+    const int64_t ih = (r / s->w) % s->h;
+    const int64_t id = (r / (s->w * s->h)) % s->d;
+    const int64_t n = r / (s->w * s->h * s->d);
+    for (int64_t c = 0; c < s->c_in; ++c) {
+      const int64_t g = c / cg;
+      double sum = 0.0;
+      for (int64_t co = g * og; co < (g + 1) * og; ++co)
+        for (int64_t kd = 0; kd < s->k_d; ++kd) {
+          const int64_t td = id + s->p_d - kd * s->e_d;
+          if (td < 0 || td % s->s_d != 0 || td / s->s_d >= od_n) continue;
+          for (int64_t kh = 0; kh < s->k_h; ++kh) {
+            const int64_t th = ih + s->p_h - kh * s->e_h;
+            if (th < 0 || th % s->s_h != 0 || th / s->s_h >= oh_n) continue;
+            for (int64_t kw = 0; kw < s->k_w; ++kw) {
+              const int64_t tw = iw + s->p_w - kw * s->e_w;
+              if (tw < 0 || tw % s->s_w != 0 || tw / s->s_w >= ow_n) continue;
+              const int64_t o = ((n * od_n + td / s->s_d) * oh_n + th / s->s_h) * ow_n + tw / s->s_w;
+              sum += dy[o * s->c_out + co] * w_at(s, wt, co, kd, kh, kw, c - g * cg);
+              macs += 1;
+            }
+          }
+        }
+      dx[r * s->c_in + c] = sum;
     }
   }
   return macs;

@@ -37,6 +37,16 @@ MUTANTS = {
     "group_channel_offset_dropped": ("g * cg + c)", "c)"),
     "group_of_output_interleaved": ("const int64_t g = co / og;", "const int64_t g = co % s->groups;"),
     "filter_channel_stride_ungrouped": ("* (s->c_in / s->groups) + c]", "* s->c_in + c]"),
+    # backward-data
+    "bwd_no_divisibility_check": ("if (td < 0 || td % s->s_d != 0 || td / s->s_d >= od_n) continue;",
+                                  "if (td < 0 || td / s->s_d >= od_n) continue;"),
+    "bwd_forward_index_sign": ("const int64_t th = ih + s->p_h - kh * s->e_h;",
+                               "const int64_t th = ih - s->p_h + kh * s->e_h;"),
+    "bwd_output_group_ignored": ("for (int64_t co = g * og; co < (g + 1) * og; ++co)",
+                                 "for (int64_t co = 0; co < og; ++co)"),
+    "bwd_dilation_ignored": ("const int64_t tw = iw + s->p_w - kw * s->e_w;",
+                             "const int64_t tw = iw + s->p_w - kw;"),
+    "bwd_high_edge_off_by_one": ("td / s->s_d >= od_n", "td / s->s_d > od_n"),
 }
 
 

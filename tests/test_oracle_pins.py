@@ -389,3 +389,110 @@ def test_all_variants_together_match_im2col_of_stuffed_padded_input():
                               for i in range(g)], axis=-1)
         assert y.shape == ref.shape, case
         np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12, err_msg=str(case))
+
+
+# --- backward-data (transposed convolution) --------------------------------------
+# Random problems over the whole descriptor: 2D and 3D, strides 1-3, low and high pads,
+# dilation, groups.  (x shape, filter extents, stride, (low, high) pads, dilation, groups, C_out)
+BWD_CASES = [
+    ((2, 5, 6, 4), (3, 3), (1, 1), ((1, 1), (1, 1)), (1, 1), 1, 3),
+    ((1, 7, 8, 4), (3, 2), (2, 3), ((1, 0), (0, 2)), (1, 1), 2, 6),
+    ((2, 5, 6, 7, 4), (3, 3, 3), (2, 2, 2), ((1, 1), (1, 1), (1, 1)), (1, 1, 1), 1, 5),
+    ((1, 6, 5, 9, 6), (2, 3, 3), (1, 2, 3), ((0, 1), (2, 0), (1, 2)), (2, 1, 2), 3, 6),
+    ((2, 9, 8, 3), (3, 3), (2, 2), ((2, 2), (2, 2)), (2, 3), 1, 2),
+    ((1, 4, 5, 6, 8), (3, 1, 2), (3, 1, 2), ((3, 3), (0, 0), (2, 1)), (1, 1, 2), 4, 4),
+]
+
+
+def _bwd_inputs(case, seed):
+    xs, ks, st, pads, dil, g, cout = case
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=xs)
+    w = rng.normal(size=(cout, *ks, xs[-1] // g))
+    return x, w
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_bwd_data_is_the_adjoint_of_the_forward_pass(case):
+    """<conv(x, w), dy> = <x, dgrad(dy, w)> for all x, dy: the defining property of the
+    gradient with respect to x (equal up to float64 rounding of two independent sums)."""
+    xs, ks, st, pads, dil, g, cout = case
+    x, w = _bwd_inputs(case, 3)
+    y = oracle.conv_fwd(x, w, st, pads, dilation=dil, groups=g)
+    dy = np.random.default_rng(4).normal(size=y.shape)
+    dx = oracle.conv_bwd_data(dy, w, xs, st, pads, dilation=dil, groups=g)
+    assert dx.shape == tuple(xs)
+    lhs, rhs = float((y * dy).sum()), float((x * dx).sum())
+    assert abs(lhs - rhs) <= 1e-10 * (abs(lhs) + np.abs(y * dy).sum())
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_bwd_data_is_a_forward_conv_of_zero_inserted_dy_with_the_flipped_filter(case):
+    """The transposed convolution as the MLX general path builds it: dy dilated by the
+    stride (zeros between neighbours), placed so that dx[i] = sum_k' B[i + k'e] wf[k'] with
+    wf the spatially flipped filter with input and output channels exchanged per group."""
+    xs, ks, st, pads, dil, g, cout = case
+    x, w = _bwd_inputs(case, 5)
+    y = oracle.conv_fwd(x, w, st, pads, dilation=dil, groups=g)
+    dy = np.random.default_rng(6).normal(size=y.shape)
+    dims = len(xs) - 2
+    big = [xs[1 + i] + dil[i] * (ks[i] - 1) for i in range(dims)]
+    B = np.zeros((xs[0], *big, cout))
+    # B index t holds dy[(t - P) / s] where P = (K-1) e - p and the division is exact
+    for idx in np.ndindex(*big):
+        src = []
+        for i in range(dims):
+            u = idx[i] - (dil[i] * (ks[i] - 1) - pads[i][0])
+            if u < 0 or u % st[i] != 0 or u // st[i] >= y.shape[1 + i]:
+                break
+            src.append(u // st[i])
+        else:
+            B[(slice(None), *idx)] = dy[(slice(None), *src)]
+    cg, og = xs[-1] // g, cout // g
+    wf = np.zeros((xs[-1], *ks, og))
+    flipped = w[(slice(None),) + (slice(None, None, -1),) * dims]
+    for gi in range(g):
+        blk = flipped[gi * og:(gi + 1) * og]                       # (og, K..., cg)
+        wf[gi * cg:(gi + 1) * cg] = np.moveaxis(blk, (0, -1), (-1, 0))
+    ref = oracle.conv_fwd(B, wf, 1, 0, dilation=dil, groups=g)
+    dx = oracle.conv_bwd_data(dy, w, xs, st, pads, dilation=dil, groups=g)
+    np.testing.assert_allclose(dx, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", BWD_CASES)
+def test_bwd_data_tap_counts_brute_force(case):
+    """dy = 1 and w = 1 only from output channel 0 to input channel 0 of group 0: dx at input
+    channel 0 counts, per position, the (tap, output) pairs that read it -- counted here by
+    running the forward index map over every output and tap."""
+    xs, ks, st, pads, dil, g, cout = case
+    y_shape = oracle.conv_fwd(np.zeros(xs), np.zeros((cout, *ks, xs[-1] // g)), st, pads,
+                              dilation=dil, groups=g).shape
+    dy = np.ones(y_shape)
+    w = np.zeros((cout, *ks, xs[-1] // g))
+    w[0, ..., 0] = 1
+    dx = oracle.conv_bwd_data(dy, w, xs, st, pads, dilation=dil, groups=g)
+    dims = len(xs) - 2
+    count = np.zeros(xs[1:-1])
+    for o in np.ndindex(*y_shape[1:-1]):
+        for k in np.ndindex(*ks):
+            i = [o[j] * st[j] - pads[j][0] + k[j] * dil[j] for j in range(dims)]
+            if all(0 <= i[j] < xs[1 + j] for j in range(dims)):
+                count[tuple(i)] += 1
+    for n in range(xs[0]):
+        np.testing.assert_array_equal(dx[n, ..., 0], count)
+    assert not dx[..., 1:].any()
+
+
+def test_bwd_data_of_the_worked_example():
+    """The tutorial's worked example (section 4): y = x * k = [[-4,-4],[-4,-4]].  With dy = 1
+    the adjoint identity gives sum(x * dx) = sum(y) = -16, and dx is the kernel summed over the
+    four output positions it was placed at."""
+    m = _read_matrices(os.path.join(GOLDEN, "worked_example_2x2_on_3x3.txt"))
+    x, k, y = m["input"], m["kernel"], m["output"]
+    dx = oracle.conv_bwd_data(np.ones((1, 2, 2, 1)), k.reshape(1, 2, 2, 1), (1, 3, 3, 1))[0, ..., 0]
+    assert float((x * dx).sum()) == float(y.sum()) == -16.0
+    placed = np.zeros((3, 3))
+    for a in range(2):
+        for b in range(2):
+            placed[a:a + 2, b:b + 2] += k
+    np.testing.assert_array_equal(dx, placed)
