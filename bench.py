@@ -38,7 +38,7 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 import implicit_gemm_conv_amd as igc  # noqa: E402
-from conv_workloads import HEADLINE, VARIANT_WORKLOADS, WORKLOADS, make_inputs  # noqa: E402
+from conv_workloads import BWD_WORKLOADS, HEADLINE, VARIANT_WORKLOADS, WORKLOADS, make_inputs  # noqa: E402
 
 PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}   # MI355X dense, published
 METRIC = "conv fwd TFLOP/s (2·M·N·K) and % of MFMA peak, fp16 NDHWC 3×3×3 shapes"
@@ -98,7 +98,10 @@ def _var(wl):
 
 def gemm_dims(wl):
     """M output positions, N = C_out, K = taps * C_in / groups: 2*M*N*K is the multiply-add
-    count of the sum (grouped layers multiply each output by one group's channels only)."""
+    count of the sum (grouped layers multiply each output by one group's channels only).
+    Backward-data performs the forward pass's multiply-adds: M is dy's positions."""
+    if wl.dx_shape is not None:
+        return int(np.prod(wl.x_shape[:-1])), wl.w_shape[0], int(np.prod(wl.w_shape[1:]))
     out = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding, **_var(wl))
     m = int(np.prod(out[:-1]))
     n = wl.w_shape[0]
@@ -139,11 +142,16 @@ def sweep(launches, names=None):
     """Per-workload event timing, warm (resident buffers) and cold (rotated buffer sets)."""
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
-    for name, wl in {**WORKLOADS, **VARIANT_WORKLOADS}.items():
+    for name, wl in {**WORKLOADS, **VARIANT_WORKLOADS, **BWD_WORKLOADS}.items():
         if names and name not in names:
             continue
-        x, w = make_inputs(wl, dev)
-        shape = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding, **_var(wl))
+        bwd = wl.dx_shape is not None
+        x, w = make_inputs(wl, dev)           # backward-data: x is dy, y is dx
+        if bwd:
+            shape = wl.dx_shape
+            wt = igc.bwd_data_filter(w, wl.dx_shape, wl.stride, wl.padding)   # once per filter
+        else:
+            shape = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding, **_var(wl))
         y = torch.empty(shape, dtype=wl.torch_dtype, device=dev)
         m, n, k = gemm_dims(wl)
         flops = 2.0 * m * n * k
@@ -159,7 +167,10 @@ def sweep(launches, names=None):
                    for _ in pairs]
             for (xi, yi), (a, b) in zip(pairs, evs):
                 a.record(stream)
-                igc.conv_fwd(xi, w, wl.stride, wl.padding, out=yi, **_var(wl))
+                if bwd:
+                    igc.conv_bwd_data(xi, w, wl.dx_shape, wl.stride, wl.padding, out=yi, wt=wt)
+                else:
+                    igc.conv_fwd(xi, w, wl.stride, wl.padding, out=yi, **_var(wl))
                 b.record(stream)
             torch.cuda.synchronize()
             return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
@@ -168,7 +179,8 @@ def sweep(launches, names=None):
         warm = timed([(x, y)] * launches)
         cold = timed([(xs[i % sets], ys[i % sets]) for i in range(launches)])
         peak = PEAK_TFLOPS[wl.dtype]
-        rec = {"workload": name, "path": kernel_key(wl), "dtype": wl.dtype, "gemm_mnk": [m, n, k],
+        rec = {"workload": name, "path": "bwd_data" if bwd else kernel_key(wl), "dtype": wl.dtype,
+               "gemm_mnk": [m, n, k],
                "gflop": round(flops / 1e9, 4), "alg_mb": round(alg_bytes / 1e6, 3), "launches": launches}
         for tag, t in (("warm", warm), ("cold", cold)):
             med = float(np.median(t))

@@ -39,6 +39,7 @@ class Workload:
     seed_w: int = 2
     dilation: tuple = None     # per dimension, None = 1 (the variants only)
     groups: int = 1            # channel groups (the variants only); w holds C_in/groups channels
+    dx_shape: tuple = None     # backward-data workloads: x_shape is dy's shape, dx_shape the result's
 
     @property
     def dims(self) -> int:
@@ -104,6 +105,19 @@ VARIANT_WORKLOADS = {
             (128, 4, 4, 64), (2, 2), ((1, 2), (1, 2))),
         replace(_wl(6, 4, "v5_conv3d_fp16_depthwise_n4_32c128", "fp16", (4, 32, 32, 32, 128),
                     (128, 3, 3, 3, 1), (1, 1, 1), ((1, 1), (1, 1), (1, 1))), groups=128),
+    ]
+}
+
+# Backward-data (the transposed convolution, "Transposed" in the tutorial's
+# variant list) of two headline layers: x_shape is dy's shape (the forward
+# output's, written out here), dx_shape the forward input's, w the forward
+# filter; stride and padding are the forward layer's.
+BWD_WORKLOADS = {
+    w.name: w for w in [
+        replace(_wl(7, 0, "d1_dgrad_conv3d_fp16_n4_32c128_o128", "fp16", (4, 32, 32, 32, 128),
+                    (128, 3, 3, 3, 128), (1, 1, 1), (1, 1, 1)), dx_shape=(4, 32, 32, 32, 128)),
+        replace(_wl(7, 1, "d2_dgrad_conv3d_fp16_n4_32c64_o128_s2", "fp16", (4, 16, 16, 16, 128),
+                    (128, 3, 3, 3, 64), (2, 2, 2), (1, 1, 1)), dx_shape=(4, 32, 32, 32, 64)),
     ]
 }
 

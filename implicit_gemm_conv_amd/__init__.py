@@ -7,6 +7,7 @@ or the tensors are not on a GPU, the call raises.
 
     import implicit_gemm_conv_amd as igc
     y = igc.conv_fwd(x, w, stride=1, padding=1)        # x (N,[D,]H,W,C), w (Co,[KD,]KH,KW,C)
+    dx = igc.conv_bwd_data(dy, w, x.shape, stride=1, padding=1)   # gradient w.r.t. x
 """
 import ctypes
 import os
@@ -58,6 +59,16 @@ EXPORTS = [
                                    ctypes.c_void_p, ctypes.c_void_p]),
     ("conv_fwd_path_ex", ctypes.c_int, [ctypes.POINTER(DescEx), ctypes.c_int, ctypes.c_void_p,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("conv_bwd_data_filter", ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]),
+    ("conv_bwd_data", ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_void_p]),
+    ("conv_bwd_data_filter_ex", ctypes.c_int, [ctypes.POINTER(DescEx), ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p]),
+    ("conv_bwd_data_ex", ctypes.c_int, [ctypes.POINTER(DescEx), ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]),
+    ("conv_bwd_data_path_ex", ctypes.c_int, [ctypes.POINTER(DescEx), ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     ("conv_strerror", ctypes.c_char_p, [ctypes.c_int]),
     ("conv_path_name", ctypes.c_char_p, [ctypes.c_int]),
 ]
@@ -188,6 +199,58 @@ def conv_fwd(x: torch.Tensor, w: torch.Tensor, stride=1, padding=0, out: torch.T
         stream = torch.cuda.current_stream(x.device).cuda_stream
         _check(lib().conv_fwd_path_ex(ctypes.byref(d), PATHS[path], x.data_ptr(), w.data_ptr(),
                                       out.data_ptr(), stream))
+    return out
+
+
+def bwd_data_filter(w: torch.Tensor, x_shape, stride=1, padding=0, dilation=1, groups: int = 1,
+                    out: torch.Tensor = None) -> torch.Tensor:
+    """The filter of the forward convolution (x_shape, w, ...) rearranged for backward-data
+    (per stride phase, taps reversed, channels exchanged); same size and dtype as w.  It
+    depends only on w and the problem, so it can be prepared once per filter."""
+    if not w.is_cuda:
+        raise ValueError("bwd_data_filter runs on the GPU only: w must be a device tensor")
+    w = w.contiguous()
+    d = make_desc_ex(tuple(x_shape), tuple(w.shape), stride, padding, dilation, groups, w.dtype)
+    if out is None:
+        out = torch.empty_like(w)
+    elif out.shape != w.shape or out.dtype != w.dtype or not out.is_contiguous() or out.device != w.device:
+        raise ValueError("out must be a contiguous tensor like w")
+    with torch.cuda.device(w.device):
+        stream = torch.cuda.current_stream(w.device).cuda_stream
+        _check(lib().conv_bwd_data_filter_ex(ctypes.byref(d), w.data_ptr(), out.data_ptr(), stream))
+    return out
+
+
+def conv_bwd_data(dy: torch.Tensor, w: torch.Tensor, x_shape, stride=1, padding=0, dilation=1,
+                  groups: int = 1, out: torch.Tensor = None, path: str = "auto",
+                  wt: torch.Tensor = None) -> torch.Tensor:
+    """Backward-data of the forward convolution (x_shape, w, stride, padding, dilation, groups):
+    dx with shape x_shape from dy with the forward output's shape (the transposed convolution
+    of dy).  w is the forward filter (C_out,[KD,]KH,KW,C_in/groups); wt, if given, is its
+    rearrangement from ``bwd_data_filter`` (else it is prepared here, a temporary the size of
+    w).  path: "auto", "main", "runs" or "direct" for the per-phase kernels.  Launched on the
+    current stream of dy's device, not synchronised."""
+    if not (dy.is_cuda and w.is_cuda):
+        raise ValueError("conv_bwd_data runs on the GPU only: dy and w must be device tensors")
+    if dy.device != w.device or dy.dtype != w.dtype:
+        raise ValueError("dy and w must share device and dtype")
+    x_shape = tuple(int(e) for e in x_shape)
+    dy = dy.contiguous()
+    y_shape = out_shape(x_shape, tuple(w.shape), stride, padding, dilation, groups)
+    if tuple(dy.shape) != y_shape:
+        raise ValueError(f"dy must have the forward output shape {y_shape}, got {tuple(dy.shape)}")
+    if wt is None:
+        wt = bwd_data_filter(w, x_shape, stride, padding, dilation, groups)
+    d = make_desc_ex(x_shape, tuple(w.shape), stride, padding, dilation, groups, dy.dtype)
+    if out is None:
+        out = torch.empty(x_shape, dtype=dy.dtype, device=dy.device)
+    elif tuple(out.shape) != x_shape or out.dtype != dy.dtype or not out.is_contiguous() \
+            or out.device != dy.device:
+        raise ValueError(f"out must be a contiguous {dy.dtype} tensor of shape {x_shape} on {dy.device}")
+    with torch.cuda.device(dy.device):
+        stream = torch.cuda.current_stream(dy.device).cuda_stream
+        _check(lib().conv_bwd_data_path_ex(ctypes.byref(d), PATHS[path], dy.data_ptr(), wt.data_ptr(),
+                                           out.data_ptr(), stream))
     return out
 
 

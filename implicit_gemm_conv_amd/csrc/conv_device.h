@@ -70,6 +70,20 @@ __device__ __forceinline__ RowInfo decode_row(const ConvParams& p, int m) {
   return r;
 }
 
+// Element offset in y of output row m (its channel 0): m * cout for a dense y,
+// else through the row strides of a stride phase of backward-data.
+__device__ __forceinline__ int64_t out_row(const ConvParams& p, int m) {
+  if (!p.remap) return (int64_t)m * p.cout;
+  const int xo = m % p.ow;
+  int t = m / p.ow;
+  const int yo = t % p.oh;
+  t /= p.oh;
+  const int zo = t % p.od;
+  const int n = t / p.od;
+  return (int64_t)p.y_off + (int64_t)n * p.ys_n + (int64_t)zo * p.ys_d + (int64_t)yo * p.ys_h +
+         (int64_t)xo * p.ys_w;
+}
+
 __device__ __forceinline__ bool tap_valid(const RowInfo& r, int kd, int kh, int kw) {
   return ((r.md >> kd) & (r.mh >> kh) & (r.mw >> kw) & 1u) != 0u;
 }

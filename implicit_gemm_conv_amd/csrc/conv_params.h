@@ -25,6 +25,13 @@ struct ConvParams {
   int ntaps;               // kd * kh * kw
   int K;                   // GEMM depth of one group: ntaps * cin_g (the filter's row length)
   int xs_w, xs_h, xs_d, xs_n;  // element strides of x along w, h, d, n (xs_w == cin)
+  // Where output row m = ((n*od + z)*oh + y)*ow + x lives in y.  remap == 0: at
+  // m * cout (y dense, the forward pass).  remap == 1: at y_off + n*ys_n +
+  // z*ys_d + y*ys_h + x*ys_w elements (one stride phase of backward-data, whose
+  // rows are every s-th position of dx).  Only the main, runs and direct
+  // kernels honour remap == 1.
+  int remap;
+  int ys_w, ys_h, ys_d, ys_n, y_off;
 };
 
 // The plain convolution: one group, undilated filter.
@@ -49,6 +56,17 @@ hipError_t launch_runs(const ConvParams& p, int dtype, const void* x, const void
                        hipStream_t s);
 hipError_t launch_grouped(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
                           hipStream_t s);
+
+// Backward-data filter rearrangement (see k_bwd.hip): per dimension the stride
+// s, dilation e, low pad p, filter extent K and, per stride phase r < s, the
+// first tap k0, the tap count T and the taps of all earlier phases pre.
+constexpr int kMaxBwdStride = 16;
+struct BwdGeom {
+  int cout, cin, groups;   // forward C_out, C_in, G
+  int k[3], s[3], e[3], p[3];
+  int k0[3][kMaxBwdStride], t[3][kMaxBwdStride], pre[3][kMaxBwdStride];
+};
+hipError_t launch_bwd_filter(const BwdGeom& g, int dtype, const void* w, void* wt, hipStream_t s);
 
 // Whether a path accepts a problem (host-side rules mirrored in convfwd.h).
 bool main_accepts(const ConvParams& p, int dtype);

@@ -93,6 +93,12 @@ int make_params(const convfwd_desc_ex* d, ConvParams* p, int64_t* x_bytes, int64
   p->xs_h = d->w * d->c_in;
   p->xs_d = d->h * d->w * d->c_in;
   p->xs_n = (int)(spatial * d->c_in);
+  p->remap = 0;
+  p->ys_w = d->c_out;
+  p->ys_h = (int)(ow * d->c_out);
+  p->ys_d = (int)(oh * ow * d->c_out);
+  p->ys_n = (int)(od * oh * ow * d->c_out);
+  p->y_off = 0;
   *x_bytes = xe * eb;
   *w_bytes = we * eb;
   *y_bytes = ye * eb;
@@ -132,6 +138,20 @@ bool path_accepts(int path, const ConvParams& p, int dtype) {
   }
 }
 
+hipError_t launch_path(int path, const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                       hipStream_t s) {
+  switch (path) {
+    case CONVFWD_PATH_MAIN: return convfwd::launch_main(p, dtype, x, w, y, s);
+    case CONVFWD_PATH_FLATK: return convfwd::launch_flatk(p, dtype, x, w, y, s);
+    case CONVFWD_PATH_ROWS: return convfwd::launch_rows(p, dtype, x, w, y, s);
+    case CONVFWD_PATH_BRICK: return convfwd::launch_brick(p, dtype, x, w, y, s);
+    case CONVFWD_PATH_STRIP: return convfwd::launch_strip(p, dtype, x, w, y, s);
+    case CONVFWD_PATH_RUNS: return convfwd::launch_runs(p, dtype, x, w, y, s);
+    case CONVFWD_PATH_GROUPED: return convfwd::launch_grouped(p, dtype, x, w, y, s);
+    default: return convfwd::launch_direct(p, dtype, x, w, y, s);
+  }
+}
+
 int run(const convfwd_desc_ex* desc, int path, const void* x, const void* w, void* y, void* stream) {
   ConvParams p;
   int64_t xb, wb, yb;
@@ -142,25 +162,211 @@ int run(const convfwd_desc_ex* desc, int path, const void* x, const void* w, voi
   if (p.n == 0) return CONVFWD_OK;  // empty batch: nothing to read or write
   if (!x || !w || !y) return CONVFWD_ERR_NULL;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb)) return CONVFWD_ERR_ALIAS;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = hipSuccess;
-  switch (path) {
-    case CONVFWD_PATH_MAIN: e = convfwd::launch_main(p, desc->dtype, x, w, y, s); break;
-    case CONVFWD_PATH_FLATK: e = convfwd::launch_flatk(p, desc->dtype, x, w, y, s); break;
-    case CONVFWD_PATH_ROWS: e = convfwd::launch_rows(p, desc->dtype, x, w, y, s); break;
-    case CONVFWD_PATH_BRICK: e = convfwd::launch_brick(p, desc->dtype, x, w, y, s); break;
-    case CONVFWD_PATH_STRIP: e = convfwd::launch_strip(p, desc->dtype, x, w, y, s); break;
-    case CONVFWD_PATH_RUNS: e = convfwd::launch_runs(p, desc->dtype, x, w, y, s); break;
-    case CONVFWD_PATH_GROUPED: e = convfwd::launch_grouped(p, desc->dtype, x, w, y, s); break;
-    default: e = convfwd::launch_direct(p, desc->dtype, x, w, y, s); break;
+  if (launch_path(path, p, desc->dtype, x, w, y, (hipStream_t)stream) != hipSuccess)
+    return CONVFWD_ERR_LAUNCH;
+  return CONVFWD_OK;
+}
+
+// ---- backward-data: stride phases (see k_bwd.hip for the derivation) ----
+
+// One dimension's share of one stride phase r: J dx positions j*s + r, the T
+// taps k0, k0 + s', ... that reach them, and the phase convolution over dy at
+// unit stride with dilation ep and low pad P (negative when the window starts
+// past the output position).
+struct PhaseDim {
+  int J, k0, T, P, ep;
+};
+
+int gcd_int(int a, int b) {
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
   }
-  if (e != hipSuccess) return CONVFWD_ERR_LAUNCH;
+  return a;
+}
+
+void phase_dims(int I, int K, int s, int p, int e, PhaseDim* out) {
+  const int g = gcd_int(e, s), sp = s / g, ep = e / g;
+  for (int r = 0; r < s; ++r) {
+    PhaseDim& d = out[r];
+    d.J = r < I ? (I - r + s - 1) / s : 0;
+    d.ep = ep;
+    d.k0 = -1;
+    for (int k = 0; k < sp; ++k)
+      if ((((k * e - r - p) % s) + s) % s == 0) {
+        d.k0 = k;
+        break;
+      }
+    if (d.k0 < 0 || d.k0 >= K) {
+      d.k0 = 0; d.T = 0; d.P = 0;
+      continue;
+    }
+    d.T = (K - d.k0 + sp - 1) / sp;
+    const int q0 = (r + p - d.k0 * e) / s;   // exact: k0*e = r + p (mod s)
+    d.P = (d.T - 1) * ep - q0;
+  }
+}
+
+struct BwdPlan {
+  ConvParams fwd;
+  int64_t x_bytes, w_bytes, y_bytes;
+  convfwd::BwdGeom geom;
+  PhaseDim ph[3][convfwd::kMaxBwdStride];
+};
+
+int make_bwd_plan(const convfwd_desc_ex* d, BwdPlan* b) {
+  const int rc = make_params(d, &b->fwd, &b->x_bytes, &b->w_bytes, &b->y_bytes);
+  if (rc != CONVFWD_OK) return rc;
+  const ConvParams& f = b->fwd;
+  const int st[3] = {f.sd, f.sh, f.sw}, ks[3] = {f.kd, f.kh, f.kw}, pads[3] = {f.pd, f.ph, f.pw};
+  const int dil[3] = {f.ed, f.eh, f.ew}, in[3] = {f.d, f.h, f.w};
+  for (int i = 0; i < 3; ++i)
+    if (st[i] > convfwd::kMaxBwdStride) return CONVFWD_ERR_UNSUPPORTED;
+  convfwd::BwdGeom& g = b->geom;
+  g.cout = f.cout; g.cin = f.cin; g.groups = f.groups;
+  for (int i = 0; i < 3; ++i) {
+    g.k[i] = ks[i]; g.s[i] = st[i]; g.e[i] = dil[i]; g.p[i] = pads[i];
+    phase_dims(in[i], ks[i], st[i], pads[i], dil[i], b->ph[i]);
+    int acc = 0;
+    for (int r = 0; r < convfwd::kMaxBwdStride; ++r) {
+      const bool live = r < st[i];
+      g.k0[i][r] = live ? b->ph[i][r].k0 : 0;
+      g.t[i][r] = live ? b->ph[i][r].T : 0;
+      g.pre[i][r] = acc;
+      if (live) acc += b->ph[i][r].T;
+    }
+  }
+  return CONVFWD_OK;
+}
+
+// The forward problem one stride phase computes: x = dy, y = the phase's dx
+// rows, filter = the phase's block of the rearranged filter.
+ConvParams phase_params(const BwdPlan& b, int rd, int rh, int rw) {
+  const ConvParams& f = b.fwd;
+  const PhaseDim& a = b.ph[0][rd];
+  const PhaseDim& c = b.ph[1][rh];
+  const PhaseDim& e = b.ph[2][rw];
+  ConvParams q;
+  q.n = f.n; q.d = f.od; q.h = f.oh; q.w = f.ow;
+  q.cin = f.cout; q.cout = f.cin;
+  q.groups = f.groups; q.cin_g = f.cout_g; q.cout_g = f.cin_g;
+  q.kd = a.T; q.kh = c.T; q.kw = e.T;
+  q.sd = q.sh = q.sw = 1;
+  q.pd = a.P; q.ph = c.P; q.pw = e.P;
+  q.ed = a.ep; q.eh = c.ep; q.ew = e.ep;
+  q.od = a.J; q.oh = c.J; q.ow = e.J;
+  q.M = f.n * a.J * c.J * e.J;
+  q.ntaps = a.T * c.T * e.T;
+  q.K = q.ntaps * q.cin_g;
+  q.xs_w = q.cin; q.xs_h = q.w * q.cin; q.xs_d = q.h * q.w * q.cin; q.xs_n = q.d * q.h * q.w * q.cin;
+  const bool unit = f.sd == 1 && f.sh == 1 && f.sw == 1;
+  q.remap = unit ? 0 : 1;
+  q.ys_w = f.sw * f.cin;
+  q.ys_h = f.sh * f.w * f.cin;
+  q.ys_d = f.sd * f.h * f.w * f.cin;
+  q.ys_n = f.d * f.h * f.w * f.cin;
+  q.y_off = (rd * f.h * f.w + rh * f.w + rw) * f.cin;
+  return q;
+}
+
+// Element offset of a phase's block in the rearranged filter.
+int64_t phase_filter_offset(const BwdPlan& b, int rd, int rh, int rw) {
+  const convfwd::BwdGeom& g = b.geom;
+  const int64_t og = b.fwd.cout_g;
+  return og * g.cin *
+         ((int64_t)g.pre[0][rd] * g.k[1] * g.k[2] + (int64_t)g.t[0][rd] * g.pre[1][rh] * g.k[2] +
+          (int64_t)g.t[0][rd] * g.t[1][rh] * g.pre[2][rw]);
+}
+
+// Path for one phase: AUTO takes the forward choice when the phase writes a
+// dense dx with non-negative pads (unit stride), else main, runs or direct,
+// the kernels that write remapped rows.  A phase without taps writes zeros
+// through the direct kernel.
+int phase_path(const ConvParams& q, int path, int dtype) {
+  if (q.ntaps == 0) return CONVFWD_PATH_DIRECT;
+  if (path != CONVFWD_PATH_AUTO) return path_accepts(path, q, dtype) ? path : -1;
+  if (!q.remap && q.pd >= 0 && q.ph >= 0 && q.pw >= 0) return auto_path(q, dtype);
+  if (convfwd::main_accepts(q, dtype)) return CONVFWD_PATH_MAIN;
+  if (convfwd::runs_accepts(q, dtype)) return CONVFWD_PATH_RUNS;
+  return CONVFWD_PATH_DIRECT;
+}
+
+int run_bwd_data(const convfwd_desc_ex* desc, int path, const void* dy, const void* wt, void* dx,
+                 void* stream) {
+  if (path != CONVFWD_PATH_AUTO && path != CONVFWD_PATH_MAIN && path != CONVFWD_PATH_RUNS &&
+      path != CONVFWD_PATH_DIRECT)
+    return CONVFWD_ERR_UNSUPPORTED;
+  BwdPlan b;
+  const int rc = make_bwd_plan(desc, &b);
+  if (rc != CONVFWD_OK) return rc;
+  const ConvParams& f = b.fwd;
+  // every phase must be runnable before the first launch
+  for (int rd = 0; rd < f.sd; ++rd)
+    for (int rh = 0; rh < f.sh; ++rh)
+      for (int rw = 0; rw < f.sw; ++rw) {
+        const ConvParams q = phase_params(b, rd, rh, rw);
+        if (q.od == 0 || q.oh == 0 || q.ow == 0) continue;
+        if (phase_path(q, path, desc->dtype) < 0) return CONVFWD_ERR_UNSUPPORTED;
+      }
+  if (f.n == 0) return CONVFWD_OK;
+  if (!dy || !wt || !dx) return CONVFWD_ERR_NULL;
+  if (overlaps(dx, b.x_bytes, dy, b.y_bytes) || overlaps(dx, b.x_bytes, wt, b.w_bytes))
+    return CONVFWD_ERR_ALIAS;
+  const int eb = elem_bytes(desc->dtype);
+  hipStream_t s = (hipStream_t)stream;
+  for (int rd = 0; rd < f.sd; ++rd)
+    for (int rh = 0; rh < f.sh; ++rh)
+      for (int rw = 0; rw < f.sw; ++rw) {
+        const ConvParams q = phase_params(b, rd, rh, rw);
+        if (q.od == 0 || q.oh == 0 || q.ow == 0) continue;
+        const char* wp = (const char*)wt + phase_filter_offset(b, rd, rh, rw) * eb;
+        if (launch_path(phase_path(q, path, desc->dtype), q, desc->dtype, dy, wp, dx, s) != hipSuccess)
+          return CONVFWD_ERR_LAUNCH;
+      }
+  return CONVFWD_OK;
+}
+
+int run_bwd_filter(const convfwd_desc_ex* desc, const void* w, void* wt, void* stream) {
+  BwdPlan b;
+  const int rc = make_bwd_plan(desc, &b);
+  if (rc != CONVFWD_OK) return rc;
+  if (!w || !wt) return CONVFWD_ERR_NULL;
+  if (overlaps(wt, b.w_bytes, w, b.w_bytes)) return CONVFWD_ERR_ALIAS;
+  if (convfwd::launch_bwd_filter(b.geom, desc->dtype, w, wt, (hipStream_t)stream) != hipSuccess)
+    return CONVFWD_ERR_LAUNCH;
   return CONVFWD_OK;
 }
 
 }  // namespace
 
 extern "C" {
+
+int conv_bwd_data_filter_ex(const convfwd_desc_ex* desc, const void* w, void* wt, void* stream) {
+  return run_bwd_filter(desc, w, wt, stream);
+}
+
+int conv_bwd_data_ex(const convfwd_desc_ex* desc, const void* dy, const void* wt, void* dx, void* stream) {
+  return run_bwd_data(desc, CONVFWD_PATH_AUTO, dy, wt, dx, stream);
+}
+
+int conv_bwd_data_path_ex(const convfwd_desc_ex* desc, int path, const void* dy, const void* wt, void* dx,
+                          void* stream) {
+  return run_bwd_data(desc, path, dy, wt, dx, stream);
+}
+
+int conv_bwd_data_filter(const convfwd_desc* desc, const void* w, void* wt, void* stream) {
+  if (!desc) return CONVFWD_ERR_NULL;
+  const convfwd_desc_ex e = widen(*desc);
+  return run_bwd_filter(&e, w, wt, stream);
+}
+
+int conv_bwd_data(const convfwd_desc* desc, const void* dy, const void* wt, void* dx, void* stream) {
+  if (!desc) return CONVFWD_ERR_NULL;
+  const convfwd_desc_ex e = widen(*desc);
+  return run_bwd_data(&e, CONVFWD_PATH_AUTO, dy, wt, dx, stream);
+}
+
 
 int conv_out_shape_ex(const convfwd_desc_ex* desc, int64_t out[5]) {
   if (!out) return CONVFWD_ERR_NULL;

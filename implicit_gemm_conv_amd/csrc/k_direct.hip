@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void conv_direct_kernel(ConvParams p, const T*
       }
     }
   }
-  y[idx] = from_f32<T>(acc);
+  y[out_row(p, m) + co] = from_f32<T>(acc);
 }
 
 hipError_t launch_direct(const ConvParams& p, int dtype, const void* x, const void* w, void* y,

@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
     const int m = m0 + row;
     const int n = n0 + k * 8;
     if (m < p.M) {
-      T* dst = y + (int64_t)m * p.cout + n;
+      T* dst = y + out_row(p, m) + n;
       if (n + 8 <= n_end) {
         if (whole16) {
           *(uint4*)dst = v;

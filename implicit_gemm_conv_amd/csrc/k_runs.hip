@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   for (int a = 0; a < FM; ++a) {
     const int m = m0 + wave * TM + a * 16 + fr;
     if (m >= p.M) continue;
-    T* yrow = y + (int64_t)m * p.cout;
+    T* yrow = y + out_row(p, m);
 #pragma unroll
     for (int b = 0; b < FN; ++b) {
       const int n = n0 + b * 16 + fg * 4;

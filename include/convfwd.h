@@ -1,6 +1,7 @@
 /*
- * convfwd.h -- C ABI of the channels-last implicit-GEMM convolution forward
- * library for AMD Instinct MI355X (gfx950).
+ * convfwd.h -- C ABI of the channels-last implicit-GEMM convolution library
+ * for AMD Instinct MI355X (gfx950): the forward pass, and backward-data (the
+ * transposed convolution) built on it.
  *
  * The operation (the "Convolutions" tutorial page, sections 1 and 4, and the
  * MLX pull request "Add implicit matmul pathway for mx.conv3d", benchmark
@@ -154,6 +155,43 @@ int conv_select_path_ex(const convfwd_desc_ex* desc);
 int conv_fwd_ex(const convfwd_desc_ex* desc, const void* x, const void* w, void* y, void* stream);
 int conv_fwd_path_ex(const convfwd_desc_ex* desc, int path, const void* x, const void* w, void* y,
                      void* stream);
+
+/* ---- Backward-data (the transposed convolution) ----
+ *
+ * The gradient with respect to x of the forward convolution `desc` (the
+ * "Transposed" entry, upsampling convolution, of the tutorial's "Convolution
+ * variants worth knowing"; the MLX pull request's general path builds it from
+ * input dilation and a flipped filter):
+ *
+ *   dx[n,id,ih,iw,c] = sum over co of c's group and taps (kd,kh,kw) with
+ *       od = (id + p_d - kd*e_d) / s_d a whole number in [0, D_out)  (likewise h, w)
+ *     of dy[n,od,oh,ow,co] * w[co,kd,kh,kw,c - g*C_in/G]
+ *
+ * dx has x's shape, dy has y's shape, w is the forward filter; positions no
+ * output window covers get 0.  A transposed convolution layer that upsamples
+ * u by stride s is this call with dy = u and desc describing the downsampling
+ * convolution whose input has the upsampled shape.  Strides up to 16 per
+ * dimension (CONVFWD_ERR_UNSUPPORTED beyond).
+ *
+ * Two calls.  conv_bwd_data_filter rearranges w into wt, a caller-owned
+ * device buffer of w's size and dtype, which must not overlap w: per stride
+ * phase (the dx positions with the same index mod s), the taps that reach it,
+ * reversed, with input and output channels exchanged.  It depends only on w
+ * and the descriptor, so it can be prepared once per filter.  conv_bwd_data
+ * then computes dx from dy and wt as s_d*s_h*s_w forward convolutions over dy
+ * (one per phase, each writing every s-th position of dx), launched in order
+ * on `stream`; dx must overlap neither dy nor wt.  Same pointer, alignment,
+ * asynchrony and error rules as conv_fwd; nothing is allocated.
+ * conv_bwd_data_path forces the kernel of the phases: CONVFWD_PATH_MAIN,
+ * CONVFWD_PATH_RUNS or CONVFWD_PATH_DIRECT (CONVFWD_ERR_UNSUPPORTED if it
+ * cannot take a phase; phases that no tap reaches are always zero-filled by
+ * the direct kernel); AUTO picks per phase. */
+int conv_bwd_data_filter(const convfwd_desc* desc, const void* w, void* wt, void* stream);
+int conv_bwd_data(const convfwd_desc* desc, const void* dy, const void* wt, void* dx, void* stream);
+int conv_bwd_data_filter_ex(const convfwd_desc_ex* desc, const void* w, void* wt, void* stream);
+int conv_bwd_data_ex(const convfwd_desc_ex* desc, const void* dy, const void* wt, void* dx, void* stream);
+int conv_bwd_data_path_ex(const convfwd_desc_ex* desc, int path, const void* dy, const void* wt, void* dx,
+                          void* stream);
 
 /* Static message for a return code; never NULL. */
 const char* conv_strerror(int code);

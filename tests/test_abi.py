@@ -239,3 +239,40 @@ def test_auto_path_for_variants():
     assert igc.select_path((2, 8, 8, 8, 96), (96, 3, 3, 3, 3), 1, 1, torch.float16, groups=32) == "runs"
     assert igc.select_path((2, 16, 16, 64), (64, 3, 3, 64), 1, 2, torch.float16, dilation=2) == "main"
     assert igc.select_path((2, 8, 8, 32, 64), (64, 3, 3, 3, 64), 1, 1, torch.float16, dilation=(2, 2, 1)) == "strip"
+
+
+# ---- backward-data entry points (host-side checks only) ---------------------------
+
+def test_bwd_data_validation_and_pointer_rules():
+    lib = igc.lib()
+    d = _desc()
+    xb, wb = 2 * 4 * 5 * 6 * 8 * 2, 4 * 27 * 8 * 2
+    base = 1 << 24
+    # the descriptor is validated first
+    assert lib.conv_bwd_data(ctypes.byref(_desc(s_h=0)), base, base, base, None) == -2
+    assert lib.conv_bwd_data_filter(ctypes.byref(_desc(k_w=0)), base, base, None) == -2
+    assert lib.conv_bwd_data(None, base, base, base, None) == -1
+    # NULL tensors
+    assert lib.conv_bwd_data(ctypes.byref(d), None, base, base + (1 << 22), None) == -1
+    assert lib.conv_bwd_data_filter(ctypes.byref(d), base, None, None) == -1
+    # dx overlapping dy or wt, wt overlapping w
+    assert lib.conv_bwd_data(ctypes.byref(d), base, base + (1 << 22), base + 64, None) == -5
+    assert lib.conv_bwd_data(ctypes.byref(d), base, base + (1 << 22), base + (1 << 22) - xb + 2, None) == -5
+    assert lib.conv_bwd_data_filter(ctypes.byref(d), base, base + wb - 2, None) == -5
+    # empty batch: nothing launched, pointers not read
+    assert lib.conv_bwd_data(ctypes.byref(_desc(n=0)), None, None, None, None) == 0
+
+
+def test_bwd_data_stride_limit_and_forced_paths():
+    lib = igc.lib()
+    ex = _desc_ex(n=0, w=40, s_w=17, k_w=3)
+    assert lib.conv_bwd_data_path_ex(ctypes.byref(ex), 0, None, None, None, None) == -3
+    assert lib.conv_bwd_data_filter_ex(ctypes.byref(ex), 16, 4096, None) == -3
+    ex = _desc_ex(n=0, w=40, s_w=16, k_w=3)
+    assert lib.conv_bwd_data_path_ex(ctypes.byref(ex), 0, None, None, None, None) == 0
+    # phases run on main, runs or direct only; main needs C_out % 32 == 0 (dy channels)
+    ex = _desc_ex(n=0, c_in=8, c_out=64, s_d=2, s_h=2, s_w=2)
+    for path, rc in ((1, 0), (7, 0), (4, 0), (2, -3), (6, -3), (3, -3), (5, -3), (8, -3)):
+        assert lib.conv_bwd_data_path_ex(ctypes.byref(ex), path, None, None, None, None) == rc, path
+    ex = _desc_ex(n=0, c_in=8, c_out=65)
+    assert lib.conv_bwd_data_path_ex(ctypes.byref(ex), 1, None, None, None, None) == -3

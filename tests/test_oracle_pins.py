@@ -496,3 +496,14 @@ def test_bwd_data_of_the_worked_example():
         for b in range(2):
             placed[a:a + 2, b:b + 2] += k
     np.testing.assert_array_equal(dx, placed)
+
+
+def test_bwd_data_rows_subset_equals_full():
+    xs, ks, st, pads, dil, g, cout = BWD_CASES[3]
+    x, w = _bwd_inputs(BWD_CASES[3], 7)
+    y = oracle.conv_fwd(x, w, st, pads, dilation=dil, groups=g)
+    dy = np.random.default_rng(8).normal(size=y.shape)
+    full = oracle.conv_bwd_data(dy, w, xs, st, pads, dilation=dil, groups=g).reshape(-1, xs[-1])
+    rows = np.array([0, 5, 17, full.shape[0] - 1])
+    part = oracle.conv_bwd_data(dy, w, xs, st, pads, dilation=dil, groups=g, rows=rows)
+    np.testing.assert_array_equal(part, full[rows])
