@@ -41,7 +41,7 @@ def _load():
                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_conv_bwd_data.restype = ctypes.c_int64
         lib.oracle_conv_bwd_data.argtypes = [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.c_void_p,
-                                             ctypes.c_void_p]
+                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.oracle_out_extent.restype = ctypes.c_int64
         lib.oracle_out_extent.argtypes = [ctypes.c_int64] * 4
         lib.oracle_out_extent_ex.restype = ctypes.c_int64
@@ -124,9 +124,10 @@ def conv_fwd(x: np.ndarray, w: np.ndarray, stride=1, padding=0, rows=None,
 
 
 def conv_bwd_data(dy: np.ndarray, w: np.ndarray, x_shape, stride=1, padding=0, dilation=1,
-                  groups: int = 1, return_macs: bool = False):
+                  groups: int = 1, return_macs: bool = False, rows=None):
     """Backward-data of the forward convolution (x_shape, w, stride, padding, dilation, groups),
-    float64: dx with shape x_shape from dy with the forward output's shape.  Arguments as for
+    float64: dx with shape x_shape from dy with the forward output's shape, or, when ``rows``
+    (flat input-position indices) is given, an array (len(rows), C_in).  Arguments as for
     ``conv_fwd``; the definition is in conv_oracle.c (the adjoint of the forward map)."""
     dy = np.ascontiguousarray(dy, dtype=np.float64)
     w = np.ascontiguousarray(w, dtype=np.float64)
@@ -148,11 +149,19 @@ def conv_bwd_data(dy: np.ndarray, w: np.ndarray, x_shape, stride=1, padding=0, d
     assert tuple(dy5.shape) == (xs5[0], *outs, w5.shape[0]), (dy5.shape, outs)
     sh = _Shape(*xs5, w5.shape[0], w5.shape[1], w5.shape[2], w5.shape[3], *st, *(p[0] for p in pp),
                 *(p[1] for p in pp), *dl, groups)
-    dx = np.zeros(xs5, dtype=np.float64)
-    macs = _load().oracle_conv_bwd_data(ctypes.byref(sh), dy5.ctypes.data, w5.ctypes.data, dx.ctypes.data)
+    if rows is None:
+        dx = np.zeros(xs5, dtype=np.float64)
+        rows_ptr, nrows = None, 0
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        dx = np.zeros((rows.shape[0], xs5[-1]), dtype=np.float64)
+        rows_ptr, nrows = rows.ctypes.data, rows.shape[0]
+    macs = _load().oracle_conv_bwd_data(ctypes.byref(sh), dy5.ctypes.data, w5.ctypes.data, rows_ptr,
+                                        nrows, dx.ctypes.data)
     if macs < 0:
-        raise ValueError("oracle rejected the shape")
-    dx = dx.reshape(x_shape)
+        raise ValueError("oracle rejected the shape or a row index")
+    if rows is None:
+        dx = dx.reshape(x_shape)
     return (dx, int(macs)) if return_macs else dx
 
 

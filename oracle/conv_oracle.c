@@ -161,10 +161,13 @@ int64_t oracle_conv_fwd(const oracle_conv_shape* s, const double* x, const doubl
 
 /*
  * Backward-data: dx (x's shape) from dy (y's shape) and the forward filter w,
- * for the forward problem *s.  Returns the number of multiply-adds done, or -1
- * for a malformed shape.
+ * for the forward problem *s.  Computes the input positions listed in `rows`
+ * (flat indices ((n*D + d)*H + h)*W + w), or all of them when rows is NULL;
+ * row r of dx receives the C_in values of rows[r].  Returns the number of
+ * multiply-adds done, or -1 for a malformed shape or an out-of-range row.
  */
-int64_t oracle_conv_bwd_data(const oracle_conv_shape* s, const double* dy, const double* wt, double* dx) {
+int64_t oracle_conv_bwd_data(const oracle_conv_shape* s, const double* dy, const double* wt,
+                             const int64_t* rows, int64_t nrows, double* dx) {
   if (s->n < 0 || s->d < 1 || s->h < 1 || s->w < 1 || s->c_in < 1 || s->c_out < 1) return -1;
   if (s->k_d < 1 || s->k_h < 1 || s->k_w < 1) return -1;
   if (s->s_d < 1 || s->s_h < 1 || s->s_w < 1) return -1;
@@ -179,14 +182,21 @@ int64_t oracle_conv_bwd_data(const oracle_conv_shape* s, const double* dy, const
   const int64_t cg = s->c_in / s->groups;
   const int64_t og = s->c_out / s->groups;
   const int64_t positions = s->n * s->d * s->h * s->w;
+  const int64_t count = rows ? nrows : positions;
+  if (count < 0) return -1;
+  if (rows) {
+    for (int64_t r = 0; r < count; ++r)
+      if (rows[r] < 0 || rows[r] >= positions) return -1;
+  }
   int64_t macs = 0;
 
 #pragma omp parallel for schedule(dynamic, 16) reduction(+ : macs)
-  for (int64_t r = 0; r < positions; ++r) {
-    const int64_t iw = r % s->w;
-    const int64_t ih = (r / s->w) % s->h;
-    const int64_t id = (r / (s->w * s->h)) % s->d;
-    const int64_t n = r / (s->w * s->h * s->d);
+  for (int64_t r = 0; r < count; ++r) {
+    const int64_t pos = rows ? rows[r] : r;
+    const int64_t iw = pos % s->w;
+    const int64_t ih = (pos / s->w) % s->h;
+    const int64_t id = (pos / (s->w * s->h)) % s->d;
+    const int64_t n = pos / (s->w * s->h * s->d);
     for (int64_t c = 0; c < s->c_in; ++c) {
       const int64_t g = c / cg;
       double sum = 0.0;
