@@ -68,6 +68,12 @@ struct BwdGeom {
 };
 hipError_t launch_bwd_filter(const BwdGeom& g, int dtype, const void* w, void* wt, hipStream_t s);
 
+// Main-path problems that share x and y and all take the main path (the
+// stride phases of backward-data), launched together: problem i reads its
+// filter w_off[i] bytes into w.
+hipError_t launch_main_phased(const ConvParams* ps, const uint32_t* w_off, int count, int dtype,
+                              const void* x, const void* w, void* y, hipStream_t s);
+
 // Whether a path accepts a problem (host-side rules mirrored in convfwd.h).
 bool main_accepts(const ConvParams& p, int dtype);
 bool flatk_accepts(const ConvParams& p, int dtype);

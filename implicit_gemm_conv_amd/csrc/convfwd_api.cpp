@@ -315,15 +315,39 @@ int run_bwd_data(const convfwd_desc_ex* desc, int path, const void* dy, const vo
     return CONVFWD_ERR_ALIAS;
   const int eb = elem_bytes(desc->dtype);
   hipStream_t s = (hipStream_t)stream;
+  // Phases on the main path share one launch (their start-up and tails
+  // overlap); the others run one launch each.
+  ConvParams batch[convfwd::kMaxBwdStride * convfwd::kMaxBwdStride];
+  uint32_t batch_off[convfwd::kMaxBwdStride * convfwd::kMaxBwdStride];
+  int nbatch = 0;
   for (int rd = 0; rd < f.sd; ++rd)
     for (int rh = 0; rh < f.sh; ++rh)
       for (int rw = 0; rw < f.sw; ++rw) {
         const ConvParams q = phase_params(b, rd, rh, rw);
         if (q.od == 0 || q.oh == 0 || q.ow == 0) continue;
-        const char* wp = (const char*)wt + phase_filter_offset(b, rd, rh, rw) * eb;
-        if (launch_path(phase_path(q, path, desc->dtype), q, desc->dtype, dy, wp, dx, s) != hipSuccess)
+        const int64_t off = phase_filter_offset(b, rd, rh, rw) * eb;
+        const int qp = phase_path(q, path, desc->dtype);
+        if (qp == CONVFWD_PATH_MAIN && q.remap && nbatch < (int)(sizeof(batch) / sizeof(batch[0]))) {
+          batch[nbatch] = q;
+          batch_off[nbatch++] = (uint32_t)off;
+          continue;
+        }
+        if (launch_path(qp, q, desc->dtype, dy, (const char*)wt + off, dx, s) != hipSuccess)
           return CONVFWD_ERR_LAUNCH;
       }
+  // Phases with more taps take longer: put them first so that the short ones
+  // fill the tail (insertion sort, at most s_d*s_h*s_w entries).
+  for (int i = 1; i < nbatch; ++i)
+    for (int j = i; j > 0 && batch[j].ntaps > batch[j - 1].ntaps; --j) {
+      const ConvParams tq = batch[j];
+      batch[j] = batch[j - 1];
+      batch[j - 1] = tq;
+      const uint32_t to = batch_off[j];
+      batch_off[j] = batch_off[j - 1];
+      batch_off[j - 1] = to;
+    }
+  if (convfwd::launch_main_phased(batch, batch_off, nbatch, desc->dtype, dy, wt, dx, s) != hipSuccess)
+    return CONVFWD_ERR_LAUNCH;
   return CONVFWD_OK;
 }
 

@@ -72,11 +72,12 @@ __device__ __forceinline__ A mfma_block(V8 a, V8 b, A c) {
   else return mfma32x32x16(a, b, c);
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int MF>
-__global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const T* __restrict__ x,
-                                                             const T* __restrict__ w,
-                                                             T* __restrict__ y, int tiles_n,
-                                                             uint32_t x_bytes, uint32_t w_bytes) {
+// One BM x BN output tile `tile` of problem p (the kernels below pick the tile
+// and the problem).
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int MF>
+__device__ __forceinline__ void main_tile(const ConvParams& p, const T* __restrict__ x,
+                                          const T* __restrict__ w, T* __restrict__ y, int tile,
+                                          int tiles_n, uint32_t x_bytes, uint32_t w_bytes) {
   // The body uses buffer-resource builtins that exist only for the GPU; the
   // host pass needs nothing but the kernel's signature to emit its launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -112,7 +113,6 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int m0 = (tile / tiles_n) * BM;
   // Column tiles never straddle a channel group: tile tn covers output
   // channels n0 .. of group g = tn / tpg, which reads input channels
@@ -270,6 +270,39 @@ __global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const
 }
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int MF>
+__global__ __launch_bounds__(256, OCC) void conv_main_kernel(ConvParams p, const T* __restrict__ x,
+                                                             const T* __restrict__ w,
+                                                             T* __restrict__ y, int tiles_n,
+                                                             uint32_t x_bytes, uint32_t w_bytes) {
+  main_tile<T, BM, BN, BK, WM, WN, STAGES, MF>(p, x, w, y, xcd_tile(blockIdx.x, gridDim.x), tiles_n,
+                                               x_bytes, w_bytes);
+}
+
+// Several problems that share x and y (the stride phases of backward-data,
+// each writing its own rows of y) in one launch: workgroups [begin[i],
+// begin[i+1]) take the tiles of problem i, whose filter starts w_off[i] bytes
+// into w.  One launch lets the phases' start-up and tail overlap.
+constexpr int kMaxPhases = 8;
+struct MainPhases {
+  int count;
+  int begin[kMaxPhases + 1];
+  int tiles_n[kMaxPhases];
+  uint32_t w_off[kMaxPhases], w_bytes[kMaxPhases];
+  ConvParams p[kMaxPhases];
+};
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int MF>
+__global__ __launch_bounds__(256, OCC) void conv_main_phased_kernel(MainPhases ph, const T* __restrict__ x,
+                                                                    const T* __restrict__ w,
+                                                                    T* __restrict__ y, uint32_t x_bytes) {
+  const int b = xcd_tile(blockIdx.x, gridDim.x);
+  int i = 0;
+  while (i + 1 < ph.count && b >= ph.begin[i + 1]) ++i;
+  main_tile<T, BM, BN, BK, WM, WN, STAGES, MF>(ph.p[i], x, (const T*)((const char*)w + ph.w_off[i]), y,
+                                               b - ph.begin[i], ph.tiles_n[i], x_bytes, ph.w_bytes[i]);
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int MF>
 hipError_t launch_cfg(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = p.groups * ((p.cout_g + BN - 1) / BN);
@@ -347,6 +380,63 @@ hipError_t launch_main(const ConvParams& p, int dtype, const void* x, const void
                        hipStream_t s) {
   if (dtype == kF16) return launch_typed<_Float16>(p, x, w, y, s);
   return launch_typed<__bf16>(p, x, w, y, s);
+}
+
+namespace {
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int MF>
+hipError_t launch_phased_cfg(const ConvParams* ps, const uint32_t* w_off, int count, const void* x,
+                             const void* w, void* y, hipStream_t s) {
+  const uint32_t xb = (uint32_t)((int64_t)ps[0].n * ps[0].xs_n * 2);
+  for (int base = 0; base < count; base += kMaxPhases) {
+    MainPhases ph;
+    ph.count = count - base < kMaxPhases ? count - base : kMaxPhases;
+    int total = 0;
+    for (int i = 0; i < ph.count; ++i) {
+      const ConvParams& p = ps[base + i];
+      const int tiles_n = p.groups * ((p.cout_g + BN - 1) / BN);
+      ph.begin[i] = total;
+      total += ((p.M + BM - 1) / BM) * tiles_n;
+      ph.tiles_n[i] = tiles_n;
+      ph.w_off[i] = w_off[base + i];
+      ph.w_bytes[i] = (uint32_t)((int64_t)p.cout * p.K * 2);
+      ph.p[i] = p;
+    }
+    ph.begin[ph.count] = total;
+    hipLaunchKernelGGL((conv_main_phased_kernel<T, BM, BN, BK, WM, WN, STAGES, OCC, MF>), dim3(total),
+                       dim3(256), 0, s, ph, (const T*)x, (const T*)w, (T*)y, xb);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// The tile choice of launch_typed, made for the phases' rows together.
+template <typename T>
+hipError_t launch_phased_typed(const ConvParams* ps, const uint32_t* w_off, int count, const void* x,
+                               const void* w, void* y, hipStream_t s) {
+  const ConvParams& p = ps[0];
+  const bool bk64 = p.cin_g % 64 == 0;
+  long rows = 0;
+  for (int i = 0; i < count; ++i) rows += ps[i].M;
+  const long tiles_256 = ((rows + 255) / 256) * p.groups * ((p.cout_g + 127) / 128);
+  if (p.cout_g <= 64 && bk64 && tiles_256 >= 256)
+    return launch_phased_cfg<T, 128, 64, 64, 2, 2, 3, 2, 16>(ps, w_off, count, x, w, y, s);
+  if (tiles_256 >= 256) {
+    if (bk64) return launch_phased_cfg<T, 128, 128, 64, 2, 2, 2, 2, 16>(ps, w_off, count, x, w, y, s);
+    return launch_phased_cfg<T, 256, 128, 32, 4, 1, 2, 2, 16>(ps, w_off, count, x, w, y, s);
+  }
+  if (bk64) return launch_phased_cfg<T, 64, 64, 64, 2, 2, 4, 2, 16>(ps, w_off, count, x, w, y, s);
+  return launch_phased_cfg<T, 128, 64, 32, 2, 2, 3, 2, 16>(ps, w_off, count, x, w, y, s);
+}
+
+}  // namespace
+
+hipError_t launch_main_phased(const ConvParams* ps, const uint32_t* w_off, int count, int dtype,
+                              const void* x, const void* w, void* y, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  if (dtype == kF16) return launch_phased_typed<_Float16>(ps, w_off, count, x, w, y, s);
+  return launch_phased_typed<__bf16>(ps, w_off, count, x, w, y, s);
 }
 
 }  // namespace convfwd
