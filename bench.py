@@ -138,8 +138,10 @@ def cpu_baseline(wls, inputs, fraction):
                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s"}
 
 
-def sweep(launches, names=None):
-    """Per-workload event timing, warm (resident buffers) and cold (rotated buffer sets)."""
+def sweep(launches, names=None, tune=False):
+    """Per-workload event timing, warm (resident buffers) and cold (rotated buffer sets).  With
+    tune, each forward shape is first timed on every path (conv_tune) and AUTO then takes the
+    fastest."""
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
     for name, wl in {**WORKLOADS, **VARIANT_WORKLOADS, **BWD_WORKLOADS}.items():
@@ -153,6 +155,8 @@ def sweep(launches, names=None):
         else:
             shape = igc.out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.padding, **_var(wl))
         y = torch.empty(shape, dtype=wl.torch_dtype, device=dev)
+        if tune and not bwd:
+            igc.tune(x, w, wl.stride, wl.padding, reps=5, out=y, **_var(wl))
         m, n, k = gemm_dims(wl)
         flops = 2.0 * m * n * k
         esz = x.element_size()
@@ -208,6 +212,8 @@ def main():
                     help="time every workload shape on its own (one JSON line each)")
     ap.add_argument("--launches", type=int, default=50, help="timed launches per shape in --sweep")
     ap.add_argument("--only", default="", help="comma-separated workload names for --sweep")
+    ap.add_argument("--tune", action="store_true",
+                    help="in --sweep, time every path per shape first and use the fastest (conv_tune)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -222,7 +228,7 @@ def main():
         copy_calibration()
         return
     if args.sweep:
-        sweep(args.launches, [n for n in args.only.split(",") if n])
+        sweep(args.launches, [n for n in args.only.split(",") if n], tune=args.tune)
         return
     wls = [WORKLOADS[n] for n in HEADLINE]
     inputs = [make_inputs(wl, dev) for wl in wls]

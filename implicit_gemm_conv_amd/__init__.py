@@ -69,6 +69,13 @@ EXPORTS = [
                                         ctypes.c_void_p, ctypes.c_void_p]),
     ("conv_bwd_data_path_ex", ctypes.c_int, [ctypes.POINTER(DescEx), ctypes.c_int, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    ("conv_tune", ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]),
+    ("conv_tune_ex", ctypes.c_int, [ctypes.POINTER(DescEx), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_float)]),
+    ("conv_tuned_path_ex", ctypes.c_int, [ctypes.POINTER(DescEx)]),
+    ("conv_tune_clear", ctypes.c_int, []),
     ("conv_strerror", ctypes.c_char_p, [ctypes.c_int]),
     ("conv_path_name", ctypes.c_char_p, [ctypes.c_int]),
 ]
@@ -200,6 +207,39 @@ def conv_fwd(x: torch.Tensor, w: torch.Tensor, stride=1, padding=0, out: torch.T
         _check(lib().conv_fwd_path_ex(ctypes.byref(d), PATHS[path], x.data_ptr(), w.data_ptr(),
                                       out.data_ptr(), stream))
     return out
+
+
+def tune(x: torch.Tensor, w: torch.Tensor, stride=1, padding=0, dilation=1, groups: int = 1,
+         reps: int = 10, out: torch.Tensor = None):
+    """Time every path (and main tile configuration) that accepts the problem, record the fastest
+    for this shape and its bucket (AUTO uses it from then on), and return (path name, mean
+    microseconds per launch).  Synchronises the current stream."""
+    if not (x.is_cuda and w.is_cuda) or x.device != w.device or x.dtype != w.dtype:
+        raise ValueError("tune needs x and w on one GPU with one dtype")
+    x = x.contiguous()
+    w = w.contiguous()
+    d = make_desc_ex(tuple(x.shape), tuple(w.shape), stride, padding, dilation, groups, x.dtype)
+    shape = out_shape(tuple(x.shape), tuple(w.shape), stride, padding, dilation, groups)
+    if out is None:
+        out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    us = ctypes.c_float(0.0)
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        path = _check(lib().conv_tune_ex(ctypes.byref(d), x.data_ptr(), w.data_ptr(), out.data_ptr(), stream,
+                                         int(reps), ctypes.byref(us)))
+    return PATH_NAMES[path], float(us.value)
+
+
+def tuned_path(x_shape, w_shape, stride=1, padding=0, dtype=torch.float16, dilation=1, groups=1):
+    """The recorded path for this problem (exact shape, then its bucket), or None."""
+    d = make_desc_ex(x_shape, w_shape, stride, padding, dilation, groups, dtype)
+    path = _check(lib().conv_tuned_path_ex(ctypes.byref(d)))
+    return PATH_NAMES[path] if path else None
+
+
+def tune_clear():
+    """Forget every recorded choice."""
+    _check(lib().conv_tune_clear())
 
 
 def bwd_data_filter(w: torch.Tensor, x_shape, stride=1, padding=0, dilation=1, groups: int = 1,

@@ -68,6 +68,13 @@ struct BwdGeom {
 };
 hipError_t launch_bwd_filter(const BwdGeom& g, int dtype, const void* w, void* wt, hipStream_t s);
 
+// The main path's tile configurations by number (0: the size-based choice of
+// launch_main); the measured selection in conv_tune times them.
+const int* main_tile_configs(int* count);
+bool main_config_accepts(const ConvParams& p, int dtype, int config);
+hipError_t launch_main_config(const ConvParams& p, int dtype, int config, const void* x, const void* w,
+                              void* y, hipStream_t s);
+
 // Main-path problems that share x and y and all take the main path (the
 // stride phases of backward-data), launched together: problem i reads its
 // filter w_off[i] bytes into w.

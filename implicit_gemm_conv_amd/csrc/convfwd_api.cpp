@@ -7,6 +7,11 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <cstring>
+#include <mutex>
+#include <unordered_map>
+
 #include "conv_params.h"
 
 using convfwd::ConvParams;
@@ -152,19 +157,171 @@ hipError_t launch_path(int path, const ConvParams& p, int dtype, const void* x, 
   }
 }
 
+// ---- measured selection: a table of timed choices keyed by the descriptor ----
+//
+// The tutorial page ("Convolutions", section 6, *Under the hood*) describes
+// the cuDNN practice: try the algorithms on a shape, cache the fastest, and
+// for varying shapes bucket the sizes.  conv_tune times every path (and every
+// main-path tile configuration) that accepts a problem and records the
+// fastest twice: under the exact descriptor and under its bucket (batch and
+// spatial extents rounded up to powers of two).  AUTO looks up the exact key,
+// then the bucket, then falls back to the size-based choice; a recorded
+// choice is used only if it accepts the problem at hand.
+
+struct TuneKey {
+  int32_t f[24];
+  bool operator==(const TuneKey& o) const { return std::memcmp(f, o.f, sizeof(f)) == 0; }
+};
+struct TuneKeyHash {
+  size_t operator()(const TuneKey& k) const {
+    uint64_t h = 1469598103934665603ull;   // FNV-1a over the key's bytes
+    const unsigned char* b = (const unsigned char*)k.f;
+    for (size_t i = 0; i < sizeof(k.f); ++i) h = (h ^ b[i]) * 1099511628211ull;
+    return (size_t)h;
+  }
+};
+struct Choice {
+  int path, config;
+  float us;
+};
+
+std::mutex& tune_mutex() {
+  static std::mutex m;
+  return m;
+}
+std::unordered_map<TuneKey, Choice, TuneKeyHash>& tune_table() {
+  static std::unordered_map<TuneKey, Choice, TuneKeyHash> t;
+  return t;
+}
+std::atomic<int>& tune_count() {
+  static std::atomic<int> c{0};
+  return c;
+}
+
+int32_t pow2_ceil(int32_t v) {
+  int32_t r = 1;
+  while (r < v && r < (1 << 30)) r <<= 1;
+  return r;
+}
+
+TuneKey tune_key(const convfwd_desc_ex& d, bool bucket) {
+  TuneKey k;
+  std::memset(&k, 0, sizeof(k));
+  const int32_t v[23] = {d.n, d.d, d.h, d.w, d.c_in, d.c_out, d.k_d, d.k_h, d.k_w, d.s_d, d.s_h, d.s_w,
+                         d.p_d, d.p_h, d.p_w, d.q_d, d.q_h, d.q_w, d.e_d, d.e_h, d.e_w, d.groups, d.dtype};
+  std::memcpy(k.f, v, sizeof(v));
+  if (bucket)
+    for (int i = 0; i < 4; ++i) k.f[i] = pow2_ceil(k.f[i]);
+  k.f[23] = bucket ? 1 : 0;
+  return k;
+}
+
+bool choice_accepts(const Choice& c, const ConvParams& p, int dtype) {
+  if (c.path == CONVFWD_PATH_MAIN) return convfwd::main_config_accepts(p, dtype, c.config);
+  return path_accepts(c.path, p, dtype);
+}
+
+// The recorded choice for the descriptor (exact key, then bucket) if it
+// accepts the problem; false when there is none.
+bool tuned_choice(const convfwd_desc_ex& d, const ConvParams& p, Choice* out) {
+  if (tune_count().load(std::memory_order_acquire) == 0) return false;
+  std::lock_guard<std::mutex> lock(tune_mutex());
+  for (int b = 0; b < 2; ++b) {
+    auto it = tune_table().find(tune_key(d, b == 1));
+    if (it != tune_table().end() && choice_accepts(it->second, p, d.dtype)) {
+      *out = it->second;
+      return true;
+    }
+  }
+  return false;
+}
+
+hipError_t launch_choice(const Choice& c, const ConvParams& p, int dtype, const void* x, const void* w,
+                         void* y, hipStream_t s) {
+  if (c.path == CONVFWD_PATH_MAIN) return convfwd::launch_main_config(p, dtype, c.config, x, w, y, s);
+  return launch_path(c.path, p, dtype, x, w, y, s);
+}
+
 int run(const convfwd_desc_ex* desc, int path, const void* x, const void* w, void* y, void* stream) {
   ConvParams p;
   int64_t xb, wb, yb;
   const int rc = make_params(desc, &p, &xb, &wb, &yb);
   if (rc != CONVFWD_OK) return rc;
-  if (path == CONVFWD_PATH_AUTO) path = auto_path(p, desc->dtype);
+  Choice tuned;
+  const bool use_tuned = path == CONVFWD_PATH_AUTO && tuned_choice(*desc, p, &tuned);
+  if (path == CONVFWD_PATH_AUTO) path = use_tuned ? tuned.path : auto_path(p, desc->dtype);
   if (!path_accepts(path, p, desc->dtype)) return CONVFWD_ERR_UNSUPPORTED;
   if (p.n == 0) return CONVFWD_OK;  // empty batch: nothing to read or write
   if (!x || !w || !y) return CONVFWD_ERR_NULL;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb)) return CONVFWD_ERR_ALIAS;
-  if (launch_path(path, p, desc->dtype, x, w, y, (hipStream_t)stream) != hipSuccess)
-    return CONVFWD_ERR_LAUNCH;
+  const hipError_t e = use_tuned ? launch_choice(tuned, p, desc->dtype, x, w, y, (hipStream_t)stream)
+                                 : launch_path(path, p, desc->dtype, x, w, y, (hipStream_t)stream);
+  if (e != hipSuccess) return CONVFWD_ERR_LAUNCH;
   return CONVFWD_OK;
+}
+
+int run_tune(const convfwd_desc_ex* desc, const void* x, const void* w, void* y, void* stream, int reps,
+             float* best_us) {
+  ConvParams p;
+  int64_t xb, wb, yb;
+  const int rc = make_params(desc, &p, &xb, &wb, &yb);
+  if (rc != CONVFWD_OK) return rc;
+  if (reps < 1 || reps > 1000) return CONVFWD_ERR_BAD_DESC;
+  if (p.n == 0) return auto_path(p, desc->dtype);   // nothing to time
+  if (!x || !w || !y) return CONVFWD_ERR_NULL;
+  if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb)) return CONVFWD_ERR_ALIAS;
+  // candidates: every accepting path, the main path once per tile configuration;
+  // the direct path only when nothing else takes the problem or it is small
+  Choice cand[64];
+  int nc = 0;
+  const int paths[] = {CONVFWD_PATH_STRIP, CONVFWD_PATH_GROUPED, CONVFWD_PATH_ROWS, CONVFWD_PATH_RUNS,
+                       CONVFWD_PATH_FLATK, CONVFWD_PATH_BRICK};
+  for (int q : paths)
+    if (path_accepts(q, p, desc->dtype)) cand[nc++] = Choice{q, 0, 0.f};
+  int ncfg = 0;
+  const int* cfgs = convfwd::main_tile_configs(&ncfg);
+  for (int i = 0; i < ncfg; ++i)
+    if (convfwd::main_config_accepts(p, desc->dtype, cfgs[i])) cand[nc++] = Choice{CONVFWD_PATH_MAIN, cfgs[i], 0.f};
+  const double macs = (double)p.M * p.cout_g * p.K;
+  if (nc == 0 || macs < 1e8) cand[nc++] = Choice{CONVFWD_PATH_DIRECT, 0, 0.f};
+
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return CONVFWD_ERR_LAUNCH;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return CONVFWD_ERR_LAUNCH;
+  }
+  int best = -1;
+  int err = CONVFWD_OK;
+  for (int i = 0; i < nc && err == CONVFWD_OK; ++i) {
+    if (launch_choice(cand[i], p, desc->dtype, x, w, y, s) != hipSuccess) { err = CONVFWD_ERR_LAUNCH; break; }
+    if (hipEventRecord(e0, s) != hipSuccess) { err = CONVFWD_ERR_LAUNCH; break; }
+    for (int r = 0; r < reps; ++r)
+      if (launch_choice(cand[i], p, desc->dtype, x, w, y, s) != hipSuccess) { err = CONVFWD_ERR_LAUNCH; break; }
+    if (err != CONVFWD_OK) break;
+    float ms = 0.f;
+    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      err = CONVFWD_ERR_LAUNCH;
+      break;
+    }
+    cand[i].us = ms * 1000.f / reps;
+    if (best < 0 || cand[i].us < cand[best].us) best = i;
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (err != CONVFWD_OK) return err;
+  // leave y holding the chosen path's result
+  if (launch_choice(cand[best], p, desc->dtype, x, w, y, s) != hipSuccess) return CONVFWD_ERR_LAUNCH;
+  {
+    std::lock_guard<std::mutex> lock(tune_mutex());
+    tune_table()[tune_key(*desc, false)] = cand[best];
+    tune_table()[tune_key(*desc, true)] = cand[best];
+    tune_count().store((int)tune_table().size(), std::memory_order_release);
+  }
+  if (best_us) *best_us = cand[best].us;
+  return cand[best].path;
 }
 
 // ---- backward-data: stride phases (see k_bwd.hip for the derivation) ----
@@ -407,7 +564,37 @@ int conv_select_path_ex(const convfwd_desc_ex* desc) {
   int64_t xb, wb, yb;
   const int rc = make_params(desc, &p, &xb, &wb, &yb);
   if (rc != CONVFWD_OK) return rc;
+  Choice c;
+  if (tuned_choice(*desc, p, &c)) return c.path;
   return auto_path(p, desc->dtype);
+}
+
+int conv_tune_ex(const convfwd_desc_ex* desc, const void* x, const void* w, void* y, void* stream, int reps,
+                 float* best_us) {
+  return run_tune(desc, x, w, y, stream, reps, best_us);
+}
+
+int conv_tune(const convfwd_desc* desc, const void* x, const void* w, void* y, void* stream, int reps,
+              float* best_us) {
+  if (!desc) return CONVFWD_ERR_NULL;
+  const convfwd_desc_ex e = widen(*desc);
+  return run_tune(&e, x, w, y, stream, reps, best_us);
+}
+
+int conv_tuned_path_ex(const convfwd_desc_ex* desc) {
+  ConvParams p;
+  int64_t xb, wb, yb;
+  const int rc = make_params(desc, &p, &xb, &wb, &yb);
+  if (rc != CONVFWD_OK) return rc;
+  Choice c;
+  return tuned_choice(*desc, p, &c) ? c.path : 0;
+}
+
+int conv_tune_clear(void) {
+  std::lock_guard<std::mutex> lock(tune_mutex());
+  tune_table().clear();
+  tune_count().store(0, std::memory_order_release);
+  return CONVFWD_OK;
 }
 
 int conv_fwd_ex(const convfwd_desc_ex* desc, const void* x, const void* w, void* y, void* stream) {

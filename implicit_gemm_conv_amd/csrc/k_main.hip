@@ -382,6 +382,23 @@ hipError_t launch_main(const ConvParams& p, int dtype, const void* x, const void
   return launch_typed<__bf16>(p, x, w, y, s);
 }
 
+const int* main_tile_configs(int* count) {
+  static const int kConfigs[] = {9, 14, 4, 3, 8, 13, 11, 10, 7, 12, 1, 43, 47, 49};
+  *count = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
+  return kConfigs;
+}
+
+bool main_config_accepts(const ConvParams& p, int dtype, int config) {
+  return main_accepts(p, dtype) && (config == 0 || p.cin_g % variant_bk(config) == 0);
+}
+
+hipError_t launch_main_config(const ConvParams& p, int dtype, int config, const void* x, const void* w,
+                              void* y, hipStream_t s) {
+  if (config == 0) return launch_main(p, dtype, x, w, y, s);
+  if (dtype == kF16) return launch_variant<_Float16>(config, p, x, w, y, s);
+  return launch_variant<__bf16>(config, p, x, w, y, s);
+}
+
 namespace {
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, int STAGES, int OCC, int MF>

@@ -38,9 +38,11 @@
  * fp32 inputs are accumulated in fp32.  The summation order is unspecified.
  *
  * Ownership: the caller owns x, w, y and the stream.  The library allocates
- * no device memory (no workspace, no im2col buffer), never frees, never
- * synchronises and keeps no mutable state, so calls are reentrant and may be
- * made from several host threads.
+ * no device memory (no workspace, no im2col buffer), never frees and never
+ * synchronises (except conv_tune, which times launches); its one piece of
+ * mutable state is the table of measured choices that conv_tune fills, guarded
+ * by a mutex, so calls are reentrant and may be made from several host
+ * threads.
  *
  * Errors: every entry point validates its arguments before touching the GPU
  * and returns 0 or one of the negative codes below.  Faults inside a kernel
@@ -155,6 +157,36 @@ int conv_select_path_ex(const convfwd_desc_ex* desc);
 int conv_fwd_ex(const convfwd_desc_ex* desc, const void* x, const void* w, void* y, void* stream);
 int conv_fwd_path_ex(const convfwd_desc_ex* desc, int path, const void* x, const void* w, void* y,
                      void* stream);
+
+/* ---- Measured selection (a table of timed choices) ----
+ *
+ * The practice the tutorial describes for cuDNN ("Convolutions", section 6,
+ * "Under the hood"): try the algorithms on a shape, keep the fastest, and for
+ * varying shapes bucket the sizes.  conv_tune times, on `stream`, every path
+ * that accepts the problem and every tile configuration of the main path (the
+ * direct path only when nothing else accepts the problem or it is small): one
+ * warm-up launch and `reps` (1..1000) timed launches each, between two HIP
+ * events, so it synchronises the stream.  It records the fastest choice in a
+ * process-wide table twice, under the exact descriptor and under its bucket
+ * (N, D, H, W rounded up to powers of two, the other fields exact), leaves y
+ * holding that choice's result and returns its path (> 0); *best_us (if not
+ * NULL) receives its mean launch time.  x, w, y as for conv_fwd; y is written
+ * many times.  With N = 0 nothing is timed and the size-based path is
+ * returned.
+ *
+ * From then on CONVFWD_PATH_AUTO (conv_fwd, conv_select_path) takes the
+ * recorded choice for the exact descriptor, else for its bucket, when that
+ * choice accepts the problem, and the size-based choice otherwise.
+ * conv_tuned_path returns the recorded path for a descriptor (exact, then
+ * bucket) or 0; conv_tune_clear empties the table.  The table is the
+ * library's only mutable state; a mutex guards it, so every call stays safe
+ * from several host threads (a lookup on an empty table takes no lock). */
+int conv_tune(const convfwd_desc* desc, const void* x, const void* w, void* y, void* stream, int reps,
+              float* best_us);
+int conv_tune_ex(const convfwd_desc_ex* desc, const void* x, const void* w, void* y, void* stream, int reps,
+                 float* best_us);
+int conv_tuned_path_ex(const convfwd_desc_ex* desc);
+int conv_tune_clear(void);
 
 /* ---- Backward-data (the transposed convolution) ----
  *

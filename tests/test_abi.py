@@ -276,3 +276,25 @@ def test_bwd_data_stride_limit_and_forced_paths():
         assert lib.conv_bwd_data_path_ex(ctypes.byref(ex), path, None, None, None, None) == rc, path
     ex = _desc_ex(n=0, c_in=8, c_out=65)
     assert lib.conv_bwd_data_path_ex(ctypes.byref(ex), 1, None, None, None, None) == -3
+
+
+# ---- measured selection table (host-side checks only) -------------------------------
+
+def test_tune_table_host_rules():
+    lib = igc.lib()
+    assert lib.conv_tune_clear() == 0
+    ex = _desc_ex()
+    assert lib.conv_tuned_path_ex(ctypes.byref(ex)) == 0            # nothing recorded
+    assert lib.conv_tuned_path_ex(ctypes.byref(_desc_ex(k_h=0))) == -2
+    us = ctypes.c_float(0)
+    base = 1 << 24
+    assert lib.conv_tune_ex(None, base, base, base, None, 5, ctypes.byref(us)) == -1
+    assert lib.conv_tune_ex(ctypes.byref(ex), base, base + (1 << 20), base + (1 << 21), None, 0, None) == -2
+    assert lib.conv_tune_ex(ctypes.byref(ex), None, base, base + (1 << 21), None, 5, None) == -1
+    assert lib.conv_tune_ex(ctypes.byref(ex), base, base + (1 << 20), base + 64, None, 5, None) == -5
+    # an empty batch times nothing and records nothing
+    empty = _desc_ex(n=0)
+    assert lib.conv_tune_ex(ctypes.byref(empty), None, None, None, None, 5, None) == \
+        lib.conv_select_path_ex(ctypes.byref(empty))
+    assert lib.conv_tuned_path_ex(ctypes.byref(empty)) == 0
+    assert igc.tuned_path((2, 4, 5, 6, 8), (4, 3, 3, 3, 8), 1, 1) is None
