@@ -273,6 +273,12 @@ VARIANTS = [
      ((0, 0), (0, 0)), (1, 1), 8),
     ("depthwise3d_fp16_dil_dh_sh2", "fp16", (1, 8, 9, 10, 24), (24, 3, 3, 3, 1), (1, 2, 1),
      ((2, 2), (2, 1), (1, 1)), (2, 2, 1), 24),
+    ("depthwise2d_bf16_k5_dh2_wide", "bf16", (2, 13, 70, 40), (40, 5, 5, 1), (1, 1),
+     ((4, 4), (2, 2)), (2, 1), 40),
+    ("depthwise3d_fp32_k3_ragged", "fp32", (2, 6, 7, 37, 12), (12, 3, 3, 3, 1), (2, 1, 1),
+     ((1, 1), (1, 1), (1, 1)), (1, 1, 1), 12),
+    ("depthwise2d_fp16_k7_c64", "fp16", (2, 20, 35, 64), (64, 7, 7, 1), (1, 1),
+     ((3, 3), (3, 3)), (1, 1), 64),
 ]
 VARIANT_PATHS = ["main", "strip", "runs", "grouped", "direct"]
 
