@@ -31,6 +31,8 @@
 // and a window row's loads gathered before its FMAs.
 #include "conv_device.h"
 
+#include <atomic>
+
 namespace convfwd {
 
 namespace {
@@ -277,17 +279,20 @@ __global__ __launch_bounds__(256) void conv_grouped_kernel(ConvParams p, const T
 
 // Workgroups the device holds at once at four waves per SIMD (one 256-thread
 // workgroup per SIMD set of a CU, four per CU), looked up once per device.
+// (Relaxed atomics: threads that race on the first lookup store the same value.)
 int resident_groups() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
-  if (cached[dev] == 0) {
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
-    cached[dev] = 4 * cus;
+    v = 4 * cus;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
 }
 
 template <typename T, int CG, int KW, int SW>
