@@ -186,12 +186,15 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
     const int wo = ((l_kd * p.kh + l_kh) * nkw + l_kw) * run + l_k0;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
-      const bool ok = live && ((a_dh[i] >> l_kd) & (a_dh[i] >> (16 + l_kh)) & (a_w[i] >> l_kw) & 1u);
+      // a piece wholly outside the row's valid columns is not loaded (reads as zero)
+      const bool ok = live && ((a_dh[i] >> l_kd) & (a_dh[i] >> (16 + l_kh)) & (a_w[i] >> l_kw) & 1u) &&
+                      a_lo[i] - l_k0 < EPC && a_hi[i] - l_k0 > 0;
       ra[slot][i] = load_piece<EB>(xr, a_e[i] + xo, ok, a_lo[i] - l_k0, a_hi[i] - l_k0, x_bytes);
     }
 #pragma unroll
     for (int j = 0; j < B_PER; ++j)
-      rb[slot][j] = load_piece<EB>(wr, b_e[j] + wo, live && b_ok[j], 0, b_hi[j] - l_k0, w_bytes);
+      rb[slot][j] = load_piece<EB>(wr, b_e[j] + wo, live && b_ok[j] && b_hi[j] - l_k0 > 0, 0, b_hi[j] - l_k0,
+                                   w_bytes);
     s_k0[slot] = l_k0;
     l_k0 += kBK;
     if (l_k0 >= run) {
@@ -222,12 +225,34 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   auto run_step = [&](int step, int slot) {
     char* st = smem + (step & 1) * STAGE;
     const int k0 = s_k0[slot];
+    // Only a piece that a valid-column boundary cuts needs masking (pieces
+    // wholly outside were not loaded); most steps of most waves have none, so
+    // the masks are skipped for the whole wave then.
+    bool cut = false;
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i)
-      *(u4*)(st + a_ldsoff[i]) = keep_range<EB>(ra[slot][i], a_lo[i] - k0, a_hi[i] - k0);
+    for (int i = 0; i < A_PER; ++i) {
+      const int jl = a_lo[i] - k0, jh = a_hi[i] - k0;
+      cut |= (jl > 0 && jl < EPC) || (jh > 0 && jh < EPC);
+    }
 #pragma unroll
-    for (int j = 0; j < B_PER; ++j)
-      if (tid + 256 * j < B_PIECES) *(u4*)(st + b_ldsoff[j]) = keep_range<EB>(rb[slot][j], 0, b_hi[j] - k0);
+    for (int j = 0; j < B_PER; ++j) {
+      const int jh = b_hi[j] - k0;
+      cut |= jh > 0 && jh < EPC;
+    }
+    if (__builtin_amdgcn_ballot_w64(cut) != 0) {
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i)
+        *(u4*)(st + a_ldsoff[i]) = keep_range<EB>(ra[slot][i], a_lo[i] - k0, a_hi[i] - k0);
+#pragma unroll
+      for (int j = 0; j < B_PER; ++j)
+        if (tid + 256 * j < B_PIECES) *(u4*)(st + b_ldsoff[j]) = keep_range<EB>(rb[slot][j], 0, b_hi[j] - k0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) *(u4*)(st + a_ldsoff[i]) = ra[slot][i];
+#pragma unroll
+      for (int j = 0; j < B_PER; ++j)
+        if (tid + 256 * j < B_PIECES) *(u4*)(st + b_ldsoff[j]) = rb[slot][j];
+    }
     // The step's pieces are visible to every wave; the LDS stage written two
     // steps from now is no longer being read.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
