@@ -9,7 +9,7 @@ the timed steps, in TFLOP/s.
 
 The JSON line also carries
   roofline:     the dominant kernel (the path with the largest share of the
-                step; the strip kernel runs both unit-stride 116-GFLOP
+                step; the slab kernel runs both unit-stride 116-GFLOP
                 convolutions) timed launch by launch with HIP events on the
                 launch stream, against the MI355X dense fp16 MFMA peak;
   cpu_baseline: the float64 CPU oracle on a bounded sample of the same
@@ -46,6 +46,8 @@ METRIC = "conv fwd TFLOP/s (2·M·N·K) and % of MFMA peak, fp16 NDHWC 3×3×3 s
 # (the stored counter figures are tied to their hash).
 _COMMON = ["implicit_gemm_conv_amd/csrc/conv_device.h", "implicit_gemm_conv_amd/csrc/conv_params.h"]
 KERNELS = {
+    "slab": ("conv_slab_kernel<fp16, K_w=3, K_h=3>: 16x32-output x 128-channel tile, 32x32x16 MFMA",
+             ["implicit_gemm_conv_amd/csrc/k_slab.hip", *_COMMON]),
     "strip": ("conv_strip_kernel<fp16, K_w=3>: 512x128 tile, 32x32x16 MFMA",
               ["implicit_gemm_conv_amd/csrc/k_strip.hip", *_COMMON]),
     "main": ("conv_main_kernel<fp16>: 128x128 tile, BK=64, 16x16x32 MFMA",
@@ -57,7 +59,7 @@ def traffic_file(path):
     return os.path.join(ROOT, "profiles", f"conv_{path}_fp16_c4ab_hbm_traffic.md")
 
 
-def kernel_source_hash(path="strip"):
+def kernel_source_hash(path="slab"):
     h = hashlib.sha256()
     for rel in KERNELS[path][1]:
         with open(os.path.join(ROOT, rel), "rb") as f:

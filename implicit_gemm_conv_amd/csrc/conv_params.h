@@ -56,6 +56,8 @@ hipError_t launch_runs(const ConvParams& p, int dtype, const void* x, const void
                        hipStream_t s);
 hipError_t launch_grouped(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
                           hipStream_t s);
+hipError_t launch_slab(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                       hipStream_t s);
 
 // Backward-data filter rearrangement (see k_bwd.hip): per dimension the stride
 // s, dilation e, low pad p, filter extent K and, per stride phase r < s, the
@@ -89,5 +91,6 @@ bool brick_accepts(const ConvParams& p, int dtype);
 bool strip_accepts(const ConvParams& p, int dtype);
 bool runs_accepts(const ConvParams& p, int dtype);
 bool grouped_accepts(const ConvParams& p, int dtype);
+bool slab_accepts(const ConvParams& p, int dtype);
 
 }  // namespace convfwd

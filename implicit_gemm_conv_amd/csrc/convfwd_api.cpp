@@ -120,8 +120,10 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
 int auto_path(const ConvParams& p, int dtype) {
   // Few channels per group (down to depthwise): the memory-bound vector-ALU form.
   if (convfwd::grouped_accepts(p, dtype)) return CONVFWD_PATH_GROUPED;
-  // The strip path wins once the w-taps share a strip (K_w >= 2); with K_w = 1
-  // it is the main path with a larger tile and the main path is faster.
+  // Once the w-taps share a strip (K_w >= 2): the slab path where the h-taps
+  // share its staged rows too, else the strip path.  With K_w = 1 the strip
+  // path is the main path with a larger tile and the main path is faster.
+  if (p.kw >= 2 && convfwd::slab_accepts(p, dtype)) return CONVFWD_PATH_SLAB;
   if (p.kw >= 2 && convfwd::strip_accepts(p, dtype)) return CONVFWD_PATH_STRIP;
   if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;
@@ -139,6 +141,7 @@ bool path_accepts(int path, const ConvParams& p, int dtype) {
     case CONVFWD_PATH_STRIP: return convfwd::strip_accepts(p, dtype);
     case CONVFWD_PATH_RUNS: return convfwd::runs_accepts(p, dtype);
     case CONVFWD_PATH_GROUPED: return convfwd::grouped_accepts(p, dtype);
+    case CONVFWD_PATH_SLAB: return convfwd::slab_accepts(p, dtype);
     default: return false;
   }
 }
@@ -153,6 +156,7 @@ hipError_t launch_path(int path, const ConvParams& p, int dtype, const void* x, 
     case CONVFWD_PATH_STRIP: return convfwd::launch_strip(p, dtype, x, w, y, s);
     case CONVFWD_PATH_RUNS: return convfwd::launch_runs(p, dtype, x, w, y, s);
     case CONVFWD_PATH_GROUPED: return convfwd::launch_grouped(p, dtype, x, w, y, s);
+    case CONVFWD_PATH_SLAB: return convfwd::launch_slab(p, dtype, x, w, y, s);
     default: return convfwd::launch_direct(p, dtype, x, w, y, s);
   }
 }
@@ -274,8 +278,8 @@ int run_tune(const convfwd_desc_ex* desc, const void* x, const void* w, void* y,
   // the direct path only when nothing else takes the problem or it is small
   Choice cand[64];
   int nc = 0;
-  const int paths[] = {CONVFWD_PATH_STRIP, CONVFWD_PATH_GROUPED, CONVFWD_PATH_ROWS, CONVFWD_PATH_RUNS,
-                       CONVFWD_PATH_FLATK, CONVFWD_PATH_BRICK};
+  const int paths[] = {CONVFWD_PATH_SLAB, CONVFWD_PATH_STRIP, CONVFWD_PATH_GROUPED, CONVFWD_PATH_ROWS,
+                       CONVFWD_PATH_RUNS, CONVFWD_PATH_FLATK, CONVFWD_PATH_BRICK};
   for (int q : paths)
     if (path_accepts(q, p, desc->dtype)) cand[nc++] = Choice{q, 0, 0.f};
   int ncfg = 0;
@@ -603,7 +607,7 @@ int conv_fwd_ex(const convfwd_desc_ex* desc, const void* x, const void* w, void*
 
 int conv_fwd_path_ex(const convfwd_desc_ex* desc, int path, const void* x, const void* w, void* y,
                      void* stream) {
-  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_GROUPED) return CONVFWD_ERR_UNSUPPORTED;
+  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_SLAB) return CONVFWD_ERR_UNSUPPORTED;
   return run(desc, path, x, w, y, stream);
 }
 
@@ -656,6 +660,7 @@ const char* conv_path_name(int path) {
     case CONVFWD_PATH_STRIP: return "strip";
     case CONVFWD_PATH_RUNS: return "runs";
     case CONVFWD_PATH_GROUPED: return "grouped";
+    case CONVFWD_PATH_SLAB: return "slab";
     default: return "unknown";
   }
 }

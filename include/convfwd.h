@@ -98,9 +98,14 @@ typedef enum {
   CONVFWD_PATH_RUNS = 7,   /* any dtype and C_in, filter <= 16 per dim (the unaligned-channel
                               tail path and fp32): the K_w * C_in columns of each (kd, kh) read
                               as one contiguous run, 16-byte unaligned pieces, MFMA */
-  CONVFWD_PATH_GROUPED = 8 /* any dtype, G > 1 with C_in/G in {1, 2, 4, 8, 16}, C_out/G <= 16 and
+  CONVFWD_PATH_GROUPED = 8, /* any dtype, G > 1 with C_in/G in {1, 2, 4, 8, 16}, C_out/G <= 16 and
                               C_out * K_d*K_h*K_w * C_in/G <= 16384 (depthwise and small groups):
                               one thread per (output position, group), fp32 FMA, filter in LDS */
+  CONVFWD_PATH_SLAB = 9    /* fp16/bf16, G = 1, C_in % 32 == 0, C_out % 4 == 0, stride and dilation 1
+                              along h and w, W_out % 32 == 0, K_h in {2, 3}, K_w <= 3, K_d <= 16:
+                              tiles of 16 output rows x 32 outputs; per (channel chunk, kd) the
+                              18 input rows those windows cover are staged in LDS once and all
+                              K_h * K_w taps read from them, MFMA */
 } convfwd_path;
 
 /* Problem descriptor.  All extents in elements. */
@@ -229,7 +234,7 @@ int conv_bwd_data_path_ex(const convfwd_desc_ex* desc, int path, const void* dy,
 const char* conv_strerror(int code);
 
 /* Static name of a path ("auto", "main", "flatk", "rows", "direct", "brick", "strip", "runs",
- * "grouped");
+ * "grouped", "slab");
  * never NULL. */
 const char* conv_path_name(int path);
 

@@ -134,21 +134,21 @@ def test_strerror_and_path_names():
     lib = igc.lib()
     for code in range(-7, 1):
         assert lib.conv_strerror(code)
-    assert [lib.conv_path_name(i).decode() for i in range(9)] == ["auto", "main", "flatk", "rows",
-                                                                  "direct", "brick", "strip", "runs",
-                                                                  "grouped"]
+    assert [lib.conv_path_name(i).decode() for i in range(10)] == ["auto", "main", "flatk", "rows",
+                                                                   "direct", "brick", "strip", "runs",
+                                                                   "grouped", "slab"]
 
 
 EXPECTED_PATHS = {
     "c1_conv3d_fp32_n1_8c16_o32": "runs",
     "c2_conv2d_fp16_n32_56c256_o256": "main",
-    "c4a_conv3d_fp16_n4_32c128_o128": "strip",
-    "c4b_conv3d_fp16_n1_64c64_o128": "strip",
+    "c4a_conv3d_fp16_n4_32c128_o128": "slab",
+    "c4b_conv3d_fp16_n1_64c64_o128": "slab",
     "c4c_conv3d_fp16_n4_32c64_o128_s2": "main",
     "c5a_conv3d_bf16_n4_32c65_o65": "runs",
     "c5b_conv3d_bf16_n4_16c21_o21": "runs",
     "c5c_conv3d_bf16_n4_32c64_o128_k311": "main",
-    "c5d_conv3d_bf16_n4_32c64_o128_k133": "strip",
+    "c5d_conv3d_bf16_n4_32c64_o128_k133": "slab",
     "c3_conv2d_fp16_stem_n64_224c3_o64_k7s2": "rows",
 }
 
@@ -225,6 +225,23 @@ def test_grouped_problem_path_acceptance(path, ok):
     and strip do not (the last returns UNSUPPORTED instead of computing something else)."""
     d = _desc_ex(n=0, c_in=128, c_out=64, groups=2, w=32, p_w=1, q_w=1)
     assert igc.lib().conv_fwd_path_ex(ctypes.byref(d), path, None, None, None, None) == (0 if ok else -3)
+
+
+# The slab path: fp16/bf16, G = 1, C_in % 32 == 0, C_out % 4 == 0, unit stride and no
+# dilation along h and w, W_out % 32 == 0, K_h in {2, 3}, K_w <= 3 (n = 0: only the rules run).
+_SLAB_OK = dict(n=0, c_in=64, c_out=68, h=9, w=32)
+@pytest.mark.parametrize("change,ok", [
+    ({}, True), ({"k_h": 2, "p_h": 0, "q_h": 0}, True), ({"k_w": 1, "p_w": 0, "q_w": 0}, True),
+    ({"dtype": 2}, True), ({"s_d": 2}, True), ({"e_d": 2}, True),
+    ({"k_h": 1, "p_h": 0, "q_h": 0}, False), ({"k_h": 4, "p_h": 2}, False), ({"k_w": 4, "p_w": 2}, False),
+    ({"s_h": 2}, False), ({"e_h": 2, "p_h": 2, "q_h": 2}, False), ({"s_w": 2, "w": 63}, False),
+    ({"w": 33}, False), ({"c_in": 48}, False), ({"c_out": 66}, False), ({"dtype": 0}, False),
+    ({"groups": 2, "c_out": 64}, False),
+])
+def test_slab_path_acceptance(change, ok):
+    d = _desc_ex(**{**_SLAB_OK, **change})
+    assert _out_shape_ex(d)[0] == 0
+    assert igc.lib().conv_fwd_path_ex(ctypes.byref(d), 9, None, None, None, None) == (0 if ok else -3)
 
 
 @pytest.mark.parametrize("path,ok", [(1, True), (7, True), (4, True), (6, False), (2, False)])

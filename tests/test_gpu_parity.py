@@ -54,8 +54,12 @@ CASES = [
     _case("strip_bf16_c96_w64_o72", "bf16", (1, 4, 5, 64, 96), (72, 3, 3, 3, 96), (1, 1, 1), (1, 1, 1), seed=22),
     _case("strip_fp16_2d_k5_o132", "fp16", (3, 9, 32, 32), (132, 5, 5, 32), (1, 1), (1, 2), seed=23),
     _case("strip_fp16_hs2_w32", "fp16", (2, 7, 9, 34, 64), (64, 3, 3, 3, 64), (2, 2, 1), (1, 0, 0), seed=24),
+    _case("slab_bf16_k2_o36_sd2", "bf16", (2, 3, 9, 33, 32), (36, 2, 2, 2, 32), (2, 1, 1), (0, 0, 0), seed=25),
+    _case("slab_fp16_2d_k3x1_o68", "fp16", (2, 21, 32, 32), (68, 3, 1, 32), (1, 1), (1, 0), seed=26),
+    _case("slab_fp16_h35_w64_two_wblocks", "fp16", (1, 2, 35, 64, 32), (64, 3, 3, 3, 32), (1, 1, 1), (1, 1, 1),
+          seed=27),
 ]
-PATHS = ["strip", "main", "brick", "rows", "runs", "flatk", "direct"]
+PATHS = ["slab", "strip", "main", "brick", "rows", "runs", "flatk", "direct"]
 
 
 def _accepts(wl, path):
@@ -67,6 +71,10 @@ def _accepts(wl, path):
         ow = (wl.x_shape[-2] + 2 * wl.padding[-1] - wl.w_shape[-2]) // wl.stride[-1] + 1
         return (half and wl.x_shape[-1] % 32 == 0 and wl.stride[-1] == 1 and ow % 32 == 0
                 and wl.w_shape[-2] <= 5)
+    if path == "slab":
+        ow = (wl.x_shape[-2] + 2 * wl.padding[-1] - wl.w_shape[-2]) // wl.stride[-1] + 1
+        return (half and wl.x_shape[-1] % 32 == 0 and wl.stride[-1] == 1 and wl.stride[-2] == 1
+                and ow % 32 == 0 and wl.w_shape[-2] <= 3 and wl.w_shape[-3] in (2, 3))
     if path == "brick":
         return half and wl.x_shape[-1] % 16 == 0 and taps >= 4
     if path == "rows":
@@ -133,6 +141,9 @@ EXACT = [
     ("main", "fp16", (2, 5, 6, 7, 64), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
     ("strip", "fp16", (2, 5, 6, 32, 64), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
     ("strip", "bf16", (1, 6, 7, 33, 32), (3, 2, 2), (2, 2, 1), (2, 1, 0)),
+    ("slab", "fp16", (2, 5, 6, 32, 64), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
+    ("slab", "bf16", (1, 6, 19, 33, 32), (3, 2, 2), (2, 1, 1), (2, 1, 0)),
+    ("slab", "fp16", (2, 3, 21, 64, 32), (1, 3, 1), (1, 1, 1), (0, 1, 0)),
     ("brick", "fp16", (2, 5, 6, 7, 64), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
     ("brick", "bf16", (1, 6, 7, 9, 32), (3, 3, 3), (2, 2, 2), (2, 1, 3)),
     ("brick", "fp16", (2, 3, 9, 40, 16), (1, 5, 3), (1, 1, 2), (0, 2, 1)),
@@ -280,7 +291,7 @@ VARIANTS = [
     ("depthwise2d_fp16_k7_c64", "fp16", (2, 20, 35, 64), (64, 7, 7, 1), (1, 1),
      ((3, 3), (3, 3)), (1, 1), 64),
 ]
-VARIANT_PATHS = ["main", "strip", "runs", "grouped", "direct"]
+VARIANT_PATHS = ["main", "slab", "strip", "runs", "grouped", "direct"]
 
 
 def _v_accepts(v, path):
@@ -296,6 +307,11 @@ def _v_accepts(v, path):
         ow = (xs[-2] + pads[-1][0] + pads[-1][1] - dil[-1] * (ws[-2] - 1) - 1) // st[-1] + 1
         return (half and g == 1 and dil[-1] == 1 and xs[-1] % 32 == 0 and ws[0] % 4 == 0
                 and st[-1] == 1 and ow % 32 == 0 and ws[-2] <= 5)
+    if path == "slab":
+        ow = (xs[-2] + pads[-1][0] + pads[-1][1] - dil[-1] * (ws[-2] - 1) - 1) // st[-1] + 1
+        return (half and g == 1 and dil[-1] == 1 and dil[-2] == 1 and xs[-1] % 32 == 0
+                and ws[0] % 4 == 0 and st[-1] == 1 and st[-2] == 1 and ow % 32 == 0
+                and ws[-2] <= 3 and ws[-3] in (2, 3))
     return True
 
 
