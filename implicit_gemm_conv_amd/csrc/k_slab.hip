@@ -22,8 +22,11 @@
 // must land by the barrier that starts the next plane; the filter slice of
 // step s + 1 goes out right after the barrier that starts step s.
 //
-// Four waves, wave v owning output rows 4v .. 4v + 3 of the tile (128 GEMM
-// rows) x 128 channels = 4 x 4 blocks of v_mfma_f32_32x32x16.  LDS: slab
+// Eight waves, two per SIMD: wave v owns output rows 4 (v % 4) .. + 3 of the
+// tile (128 GEMM rows) x channels 64 (v / 4) .. + 63 = 4 x 2 blocks of
+// v_mfma_f32_32x32x16, 128 accumulator registers, so that the two waves of a
+// SIMD cover each other's barrier waits and fragment-read latency (one wave
+// per SIMD with a 128 x 128 block ran 5-9% slower on the same loads).  LDS: slab
 // position o of row r at (36 r + o) * 64 bytes, its four 16-byte channel
 // chunks XOR-swizzled by bits 2..3 of o (the same for every row), so fragment
 // addresses are per-lane constants plus immediates, and one 256-byte LDS pass
@@ -52,12 +55,12 @@ constexpr int kMaxKW = 3;
 constexpr int kMaxKH = 3;
 constexpr int kRowsIn = kRowsOut + kMaxKH - 1;      // 18 slab rows
 constexpr int kRowB = 64;                           // bytes per position / filter row (32 channels)
-constexpr int kA_LOADS = 11;                        // 16-position wave loads per wave per slab
-constexpr int kSlabBytes = 4 * kA_LOADS * 16 * kRowB;   // 44 KB (18 x 36 positions and a spare tail)
+constexpr int kA_LOADS = 6;                         // 16-position wave loads per wave per slab
+constexpr int kSlabBytes = 8 * kA_LOADS * 16 * kRowB;   // 48 KB (18 x 36 positions and a spare tail)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kOutRowB = kBN * 2;
 constexpr int kOutTileBytes = kBM * kOutRowB;       // 128 KB
-static_assert(4 * kA_LOADS * 16 >= kRowsIn * kSW, "slab loads cover the slab");
+static_assert(8 * kA_LOADS * 16 >= kRowsIn * kSW, "slab loads cover the slab");
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
@@ -79,7 +82,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 __device__ __forceinline__ int swz(int o, int c) { return c ^ ((o >> 2) & 3); }
 
 template <typename T, int KW, int KH>
-__global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T* __restrict__ x,
+__global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T* __restrict__ x,
                                                            const T* __restrict__ w,
                                                            T* __restrict__ y, int tiles_n,
                                                            uint32_t x_bytes, uint32_t w_bytes) {
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
   typedef typename Vec8<T>::type V8;
   constexpr int B_ROWS = KW * kBN;                 // filter rows per step
   constexpr int B_BYTES = B_ROWS * kRowB;
-  constexpr int B_LOADS = B_ROWS * 4 / 256;        // 16-byte pieces per thread
+  constexpr int B_LOADS = B_ROWS * 4 / 512;        // 16-byte pieces per thread
   static_assert(KW >= 1 && KW <= kMaxKW && KH >= 2 && KH <= kMaxKH, "filter extents");
   constexpr int B_BASE = 2 * kSlabBytes;
   constexpr int RING = B_BASE + 2 * B_BYTES;
@@ -98,6 +101,7 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 3, wn = wave >> 2;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int n0 = (tile % tiles_n) * kBN;
   // tile rows: w-block fastest, then h-block, depth, image
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
   const __amdgpu_buffer_rsrc_t wr =
       __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, (int)w_bytes, kRawBufferFlags);
 
-  // ---- slab loader: wave load i = 4 q + wave fills positions 16 i .. 16 i + 15
+  // ---- slab loader: wave load i = 8 q + wave fills positions 16 i .. 16 i + 15
   // (four lanes each, one 16-byte chunk per lane); this lane's row, position
   // and chunk.  Validity along h and w is fixed per lane; along depth it is a
   // bit mask over kd. ----
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
   const uint32_t dmask = dim_mask(z0, p.kd, p.d, p.ed);
 #pragma unroll
   for (int q = 0; q < kA_LOADS; ++q) {
-    const int pos = (4 * q + wave) * 16 + (lane >> 2);
+    const int pos = (8 * q + wave) * 16 + (lane >> 2);
     const int r = pos / kSW, o = pos - (pos / kSW) * kSW;
     const int c = swz(o, lane & 3);                    // logical chunk this lane fetches
     const int ih = y0 + r, iw = x0 + o;
@@ -139,11 +143,11 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
     a_base[q] = base;
     a_mask[q] = mask;
   }
-  // ---- filter loader: piece j = 256 s + tid -> (tap kw, row n, physical chunk) ----
+  // ---- filter loader: piece j = 512 s + tid -> (tap kw, row n, physical chunk) ----
   uint32_t b_base[B_LOADS];
 #pragma unroll
   for (int s = 0; s < B_LOADS; ++s) {
-    const int j = s * 256 + tid;
+    const int j = s * 512 + tid;
     const int row = j >> 2, phys = j & 3;     // row = kw * 128 + n
     const int kw = row / kBN, n = row % kBN;
     const int c = swz(row, phys);
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
     for (int q = q0; q < q1; ++q) {
       const bool ok = (((a_mask[q] & live) >> a_kd) & 1u) != 0u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (lds_ptr_t)(sa + ((4 * q + wave) * 16) * kRowB), 16, ok ? a_base[q] + xoff : kOutOfRange,
+          xr, (lds_ptr_t)(sa + ((8 * q + wave) * 16) * kRowB), 16, ok ? a_base[q] + xoff : kOutOfRange,
           0, 0, 0);
     }
     if (q1 == kA_LOADS) {
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
 #pragma unroll
     for (int s = 0; s < B_LOADS; ++s)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wr, (lds_ptr_t)(sb + (s * 256 + wave * 64) * 16), 16, (b_base[s] + woff) | (~live & kOutOfRange), 0,
+          wr, (lds_ptr_t)(sb + (s * 512 + wave * 64) * 16), 16, (b_base[s] + woff) | (~live & kOutOfRange), 0,
           0, 0);
     const int h1 = b_kh + 1;
     const bool wh = h1 == KH;
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
   };
 
   // ---- fragment addresses: lane (r = lane % 32, g2 = lane / 32); tile row
-  // 4 wave + a reads slab row 4 wave + a + kh ----
+  // 4 wm + a reads slab row 4 wm + a + kh ----
   const int r = lane & 31, g2 = lane >> 5;
   int a_addr[KW][2], b_addr[2];
 #pragma unroll
@@ -204,37 +208,37 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int o = r + kw;
-      a_addr[kw][ks] = (wave * 4 * kSW + o) * kRowB + swz(o, 2 * ks + g2) * 16;
+      a_addr[kw][ks] = (wm * 4 * kSW + o) * kRowB + swz(o, 2 * ks + g2) * 16;
     }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) b_addr[ks] = r * kRowB + swz(r, 2 * ks + g2) * 16;
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-  // A step is 2 K_w blocks (tap kw, k-half ks) of 16 MFMAs.  Block j+1's
+  // A step is 2 K_w blocks (tap kw, k-half ks) of 8 MFMAs per wave.  Block j+1's
   // fragments are read while block j's MFMAs run; the step's last block
   // passes the barrier first and reads the next step's first fragments.
   constexpr int NBLK = 2 * KW;
   constexpr int USLOTS = (KH - 1) * (NBLK - 1);   // blocks that carry slab pieces
-  V8 fa[2][4], fb[2][4];
-  auto read_block = [&](V8(&af)[4], V8(&bf)[4], const char* sa, const char* sb, int kw, int ks)
+  V8 fa[2][4], fb[2][2];
+  auto read_block = [&](V8(&af)[4], V8(&bf)[2], const char* sa, const char* sb, int kw, int ks)
       __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) af[a] = *(const V8*)(sa + a_addr[kw][ks] + a * kSW * kRowB);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) bf[b] = *(const V8*)(sb + b_addr[ks] + (kw * kBN + b * 32) * kRowB);
+    for (int b = 0; b < 2; ++b) bf[b] = *(const V8*)(sb + b_addr[ks] + (kw * kBN + wn * 64 + b * 32) * kRowB);
   };
-  auto mma_block = [&](const V8(&af)[4], const V8(&bf)[4]) __attribute__((always_inline)) {
+  auto mma_block = [&](const V8(&af)[4], const V8(&bf)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = mfma32x32x16(bf[b], af[a], acc[a][b]);
+      for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16(bf[b], af[a], acc[a][b]);
   };
   // Step kh of a slab on (sa = slab stage + kh rows, sb); unless it is the
   // last, hand over to (na, nb).  At its closing barrier the filter of the
@@ -257,11 +261,11 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
           issue_a_part((u * kA_LOADS) / USLOTS, ((u + 1) * kA_LOADS) / USLOTS);
         }
         mma_block(fa[cur], fb[cur]);
-        // in the shadow of each MFMA: a fragment read (first 8), address VALU, a load
+        // in the shadow of each MFMA: a fragment read (first 6), address VALU, a load
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
@@ -274,11 +278,11 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
         issue_b();                          // the step after next, into this step's filter stage
         mma_block(fa[cur], fb[cur]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, (B_LOADS + 15) / 16, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, (B_LOADS + 7) / 8, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       } else {
@@ -317,31 +321,34 @@ __global__ __launch_bounds__(256, 1) void conv_slab_kernel(ConvParams p, const T
   }
 
   // ---- epilogue: the tile goes through LDS so each store writes whole
-  // 16-byte pieces of output rows.  Lane (r, g2) holds tile rows 32 a + r of
-  // this wave and channels 32 b + 8 q + 4 g2 + i; in LDS a row is 256 bytes,
-  // its 16-byte piece k at slot k ^ (row % 16).  Wait for the zero-fill loads
+  // 16-byte pieces of output rows.  Lane (r, g2) holds tile rows
+  // 32 (4 wm + a) + r and channels 64 wn + 32 b + 8 q + 4 g2 + i; in LDS a row
+  // is 256 bytes, its 16-byte piece k at slot k ^ (row % 16); after a barrier
+  // the workgroup stores the whole tile.  Wait for the zero-fill loads
   // past the end and for every wave's last reads first. ----
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  char* ep = smem + wave * (kOutTileBytes / 4);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = a * 32 + r;
+        const int row = (wm * 4 + a) * 32 + r;
+        const int k = wn * 8 + 4 * b + q;
         union { T h[4]; uint2 u; } pk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[a][b][4 * q + i]);
-        *(uint2*)(ep + row * kOutRowB + (((4 * b + q) ^ (row & 15)) * 16) + g2 * 8) = pk.u;
+        *(uint2*)(smem + row * kOutRowB + ((k ^ (row & 15)) * 16) + g2 * 8) = pk.u;
       }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const bool whole16 = (p.cout & 7) == 0;   // 16-byte stores stay aligned
   const int64_t plane = (int64_t)(img * p.od + od) * p.oh;
 #pragma unroll 4
-  for (int i = 0; i < kBM / 4 / 4; ++i) {
-    const int row = 4 * i + (lane >> 4), k = lane & 15;
-    const uint4 v = *(const uint4*)(ep + row * kOutRowB + ((k ^ (row & 15)) * 16));
-    const int oh = oh0 + wave * 4 + (row >> 5);
+  for (int i = 0; i < kBM * 16 / 512; ++i) {
+    const int piece = i * 512 + tid;
+    const int row = piece >> 4, k = piece & 15;
+    const uint4 v = *(const uint4*)(smem + row * kOutRowB + ((k ^ (row & 15)) * 16));
+    const int oh = oh0 + (row >> 5);
     const int n = n0 + k * 8;
     if (oh < p.oh) {
       const int64_t m = (plane + oh) * p.ow + ow0 + (row & 31);
@@ -367,7 +374,7 @@ hipError_t launch_k(const ConvParams& p, const void* x, const void* w, void* y, 
   const int tiles_n = (p.cout + kBN - 1) / kBN;
   const uint32_t xb = (uint32_t)((int64_t)p.n * p.xs_n * 2);
   const uint32_t wb = (uint32_t)((int64_t)p.cout * p.K * 2);
-  hipLaunchKernelGGL((conv_slab_kernel<T, KW, KH>), dim3(tiles_m * tiles_n), dim3(256), 0, s, p,
+  hipLaunchKernelGGL((conv_slab_kernel<T, KW, KH>), dim3(tiles_m * tiles_n), dim3(512), 0, s, p,
                      (const T*)x, (const T*)w, (T*)y, tiles_n, xb, wb);
   return hipGetLastError();
 }
