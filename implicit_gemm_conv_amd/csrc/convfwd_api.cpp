@@ -123,7 +123,12 @@ int auto_path(const ConvParams& p, int dtype) {
   // Once the w-taps share a strip (K_w >= 2): the slab path where the h-taps
   // share its staged rows too, else the strip path.  With K_w = 1 the strip
   // path is the main path with a larger tile and the main path is faster.
-  if (p.kw >= 2 && convfwd::slab_accepts(p, dtype)) return CONVFWD_PATH_SLAB;
+  // The slab path computes whole blocks of 16 rows x 32 outputs; it is taken
+  // when at least 70% of that area lies inside the output (on (32,56^2,256)
+  // with 77% it runs 1.17x faster than the main path).
+  const int64_t wpad = (p.ow + 31) / 32 * 32, hpad = (p.oh + 15) / 16 * 16;
+  if (p.kw >= 2 && 10 * (int64_t)p.ow * p.oh >= 7 * wpad * hpad && convfwd::slab_accepts(p, dtype))
+    return CONVFWD_PATH_SLAB;
   if (p.kw >= 2 && convfwd::strip_accepts(p, dtype)) return CONVFWD_PATH_STRIP;
   if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;

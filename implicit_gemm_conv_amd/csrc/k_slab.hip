@@ -1,13 +1,14 @@
 // k_slab.hip -- implicit GEMM whose K steps read the w-taps and the h-taps of
 // a filter plane from one staged block of input rows (fp16/bf16, C_in % 32 ==
-// 0, unit stride and no dilation along h and w, W_out % 32 == 0, K_h in
-// {2, 3}, K_w <= 3).
+// 0, unit stride and no dilation along h and w, K_h in {2, 3}, K_w <= 3).
 //
 // The classic implicit GEMM ("Convolutions" tutorial, section 5) gathers the
 // A tile of every tap afresh, although the tiles of neighbouring taps are the
 // same input values moved by one position.  Here a tile is 16 consecutive
 // output rows along h times 32 consecutive outputs along w (512 GEMM rows, one
-// depth plane of one image) and 128 output channels.  For one (channel chunk
+// depth plane of one image; the last tiles along h and w may hang over the
+// output's end, their extra rows computed on zeros and not stored) and 128
+// output channels.  For one (channel chunk
 // of 32, kd) the workgroup stages the 18 input rows x 34 positions that the
 // tile's windows cover (a "slab", rows padded to 36 positions, zeros outside
 // the input); output row g of the tile reads slab row g + kh for tap kh and
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int n0 = (tile % tiles_n) * kBN;
   // tile rows: w-block fastest, then h-block, depth, image
-  const int wblocks = p.ow / kSeg, hblocks = (p.oh + kRowsOut - 1) / kRowsOut;
+  const int wblocks = (p.ow + kSeg - 1) / kSeg, hblocks = (p.oh + kRowsOut - 1) / kRowsOut;
   int t = tile / tiles_n;
   const int ow0 = (t % wblocks) * kSeg;
   t /= wblocks;
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
     const uint4 v = *(const uint4*)(smem + row * kOutRowB + ((k ^ (row & 15)) * 16));
     const int oh = oh0 + (row >> 5);
     const int n = n0 + k * 8;
-    if (oh < p.oh) {
+    if (oh < p.oh && ow0 + (row & 31) < p.ow) {
       const int64_t m = (plane + oh) * p.ow + ow0 + (row & 31);
       T* dst = y + m * p.cout + n;
       if (n + 8 <= p.cout) {
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
 
 template <typename T, int KW, int KH>
 hipError_t launch_k(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
-  const int tiles_m = p.n * p.od * ((p.oh + kRowsOut - 1) / kRowsOut) * (p.ow / kSeg);
+  const int tiles_m = p.n * p.od * ((p.oh + kRowsOut - 1) / kRowsOut) * ((p.ow + kSeg - 1) / kSeg);
   const int tiles_n = (p.cout + kBN - 1) / kBN;
   const uint32_t xb = (uint32_t)((int64_t)p.n * p.xs_n * 2);
   const uint32_t wb = (uint32_t)((int64_t)p.cout * p.K * 2);
@@ -398,7 +399,7 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
 bool slab_accepts(const ConvParams& p, int dtype) {
   return (dtype == kF16 || dtype == kBF16) && p.groups == 1 && p.remap == 0 && p.sh == 1 &&
          p.sw == 1 && p.eh == 1 && p.ew == 1 && p.cin % 32 == 0 && p.cout % 4 == 0 &&
-         p.ow % kSeg == 0 && p.kw <= kMaxKW && p.kh >= 2 && p.kh <= kMaxKH && p.kd <= 16;
+         p.kw <= kMaxKW && p.kh >= 2 && p.kh <= kMaxKH && p.kd <= 16;
 }
 
 hipError_t launch_slab(const ConvParams& p, int dtype, const void* x, const void* w, void* y,

@@ -102,8 +102,8 @@ typedef enum {
                               C_out * K_d*K_h*K_w * C_in/G <= 16384 (depthwise and small groups):
                               one thread per (output position, group), fp32 FMA, filter in LDS */
   CONVFWD_PATH_SLAB = 9    /* fp16/bf16, G = 1, C_in % 32 == 0, C_out % 4 == 0, stride and dilation 1
-                              along h and w, W_out % 32 == 0, K_h in {2, 3}, K_w <= 3, K_d <= 16:
-                              tiles of 16 output rows x 32 outputs; per (channel chunk, kd) the
+                              along h and w, K_h in {2, 3}, K_w <= 3, K_d <= 16: tiles of 16
+                              output rows x 32 outputs (ragged at the ends); per (channel chunk, kd) the
                               18 input rows those windows cover are staged in LDS once and all
                               K_h * K_w taps read from them, MFMA */
 } convfwd_path;

@@ -141,7 +141,7 @@ def test_strerror_and_path_names():
 
 EXPECTED_PATHS = {
     "c1_conv3d_fp32_n1_8c16_o32": "runs",
-    "c2_conv2d_fp16_n32_56c256_o256": "main",
+    "c2_conv2d_fp16_n32_56c256_o256": "slab",
     "c4a_conv3d_fp16_n4_32c128_o128": "slab",
     "c4b_conv3d_fp16_n1_64c64_o128": "slab",
     "c4c_conv3d_fp16_n4_32c64_o128_s2": "main",
@@ -235,7 +235,7 @@ _SLAB_OK = dict(n=0, c_in=64, c_out=68, h=9, w=32)
     ({"dtype": 2}, True), ({"s_d": 2}, True), ({"e_d": 2}, True),
     ({"k_h": 1, "p_h": 0, "q_h": 0}, False), ({"k_h": 4, "p_h": 2}, False), ({"k_w": 4, "p_w": 2}, False),
     ({"s_h": 2}, False), ({"e_h": 2, "p_h": 2, "q_h": 2}, False), ({"s_w": 2, "w": 63}, False),
-    ({"w": 33}, False), ({"c_in": 48}, False), ({"c_out": 66}, False), ({"dtype": 0}, False),
+    ({"w": 33}, True), ({"w": 7}, True), ({"c_in": 48}, False), ({"c_out": 66}, False), ({"dtype": 0}, False),
     ({"groups": 2, "c_out": 64}, False),
 ])
 def test_slab_path_acceptance(change, ok):

@@ -58,6 +58,8 @@ CASES = [
     _case("slab_fp16_2d_k3x1_o68", "fp16", (2, 21, 32, 32), (68, 3, 1, 32), (1, 1), (1, 0), seed=26),
     _case("slab_fp16_h35_w64_two_wblocks", "fp16", (1, 2, 35, 64, 32), (64, 3, 3, 3, 32), (1, 1, 1), (1, 1, 1),
           seed=27),
+    _case("slab_fp16_2d_w56_ragged", "fp16", (2, 12, 56, 64), (64, 3, 3, 64), (1, 1), (1, 1), seed=28),
+    _case("slab_bf16_w9_narrow", "bf16", (1, 3, 5, 9, 32), (40, 2, 2, 3, 32), (1, 1, 1), (0, 0, 1), seed=29),
 ]
 PATHS = ["slab", "strip", "main", "brick", "rows", "runs", "flatk", "direct"]
 
@@ -72,9 +74,8 @@ def _accepts(wl, path):
         return (half and wl.x_shape[-1] % 32 == 0 and wl.stride[-1] == 1 and ow % 32 == 0
                 and wl.w_shape[-2] <= 5)
     if path == "slab":
-        ow = (wl.x_shape[-2] + 2 * wl.padding[-1] - wl.w_shape[-2]) // wl.stride[-1] + 1
         return (half and wl.x_shape[-1] % 32 == 0 and wl.stride[-1] == 1 and wl.stride[-2] == 1
-                and ow % 32 == 0 and wl.w_shape[-2] <= 3 and wl.w_shape[-3] in (2, 3))
+                and wl.w_shape[-2] <= 3 and wl.w_shape[-3] in (2, 3))
     if path == "brick":
         return half and wl.x_shape[-1] % 16 == 0 and taps >= 4
     if path == "rows":
@@ -308,9 +309,8 @@ def _v_accepts(v, path):
         return (half and g == 1 and dil[-1] == 1 and xs[-1] % 32 == 0 and ws[0] % 4 == 0
                 and st[-1] == 1 and ow % 32 == 0 and ws[-2] <= 5)
     if path == "slab":
-        ow = (xs[-2] + pads[-1][0] + pads[-1][1] - dil[-1] * (ws[-2] - 1) - 1) // st[-1] + 1
         return (half and g == 1 and dil[-1] == 1 and dil[-2] == 1 and xs[-1] % 32 == 0
-                and ws[0] % 4 == 0 and st[-1] == 1 and st[-2] == 1 and ow % 32 == 0
+                and ws[0] % 4 == 0 and st[-1] == 1 and st[-2] == 1
                 and ws[-2] <= 3 and ws[-3] in (2, 3))
     return True
 
