@@ -11,7 +11,8 @@ The JSON line also carries
   roofline:     the dominant kernel (the path with the largest share of the
                 step; the slab kernel runs both unit-stride 116-GFLOP
                 convolutions) timed launch by launch with HIP events on the
-                launch stream, against the MI355X dense fp16 MFMA peak;
+                launch stream (one before each launch, each launch timed to
+                the next event), against the MI355X dense fp16 MFMA peak;
   cpu_baseline: the float64 CPU oracle on a bounded sample of the same
                 workload (a fixed set of output rows of the first convolution),
                 on this host's cores, rank 0 only.
@@ -241,22 +242,22 @@ def main():
     step_flops = sum(flops)
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
+    def step(marks=None):
         for i, wl in enumerate(wls):
             x, w = inputs[i]
-            if events is not None:
-                events[i][0].record(stream)
+            if marks is not None:
+                marks[i].record(stream)
             igc.conv_fwd(x, w, wl.stride, wl.padding, out=outs[i])
-            if events is not None:
-                events[i][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # Timed region: exactly `steps` steps between two synchronisations.
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in wls] for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps between two synchronisations.  One HIP
+    # event goes on the launch stream before every launch (and one after the
+    # last), so each launch is timed from its own event to the next one: one
+    # event per launch instead of a pair (each event costs the stream a few us).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in wls] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -268,9 +269,13 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
+    def launch_ms(s, i):
+        nxt = ev[s][i + 1] if i + 1 < len(wls) else (ev[s + 1][0] if s + 1 < args.steps else t_end)
+        return ev[s][i].elapsed_time(nxt)
+
     per = {}
     for i, wl in enumerate(wls):
-        times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        times = [launch_ms(s, i) for s in range(args.steps)]
         us = 1e3 * float(np.mean(times))
         per[wl.name] = {"path": kernel_key(wl), "us_mean": round(us, 3),
                         "us_min": round(1e3 * float(np.min(times)), 3),
@@ -282,8 +287,7 @@ def main():
     share = {k: sum(per[wl.name]["us_mean"] for wl, kk in zip(wls, keys) if kk == k) for k in set(keys)}
     dom_path = max(share, key=share.get)
     dom = [i for i, k in enumerate(keys) if k == dom_path]
-    dom_us = float(np.mean([1e3 * ev[s][i][0].elapsed_time(ev[s][i][1])
-                            for s in range(args.steps) for i in dom]))
+    dom_us = float(np.mean([1e3 * launch_ms(s, i) for s in range(args.steps) for i in dom]))
     dom_flops = float(np.mean([flops[i] for i in dom]))
     achieved = dom_flops / (dom_us * 1e-6) / 1e12
     alg_bytes = [2 * (int(np.prod(wl.x_shape)) + int(np.prod(wl.w_shape)) +
