@@ -88,6 +88,16 @@ __device__ __forceinline__ bool tap_valid(const RowInfo& r, int kd, int kh, int 
   return ((r.md >> kd) & (r.mh >> kh) & (r.mw >> kw) & 1u) != 0u;
 }
 
+// ---- output stores ----
+// A 16-byte non-temporal store: output tiles are written once and not read
+// back by the kernel, and a whole grid storing its tiles at once writes
+// faster this way than through the ordinary write-allocate path (1-9% per
+// launch on the measured shapes).
+__device__ __forceinline__ void store16_nt(void* dst, uint4 v) {
+  const u32x4_t vv = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(vv, (u32x4_t*)dst);
+}
+
 // ---- XCD-aware tile order ----
 // Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
 // Give each XCD one contiguous run of tile ids so that the tiles resident on

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256, 4) void conv_grouped_tiled_kernel(ConvParams p
         T out[VE];
 #pragma unroll
         for (int j = 0; j < VE; ++j) out[j] = from_f32<T>(acc[t][j]);
-        *(u4*)(yrow + (int64_t)(ow0 + t) * p.cout) = __builtin_bit_cast(u4, out);
+        store16_nt(yrow + (int64_t)(ow0 + t) * p.cout, __builtin_bit_cast(uint4, out));
       }
     }
   }

@@ -256,7 +256,7 @@ __device__ __forceinline__ void main_tile(const ConvParams& p, const T* __restri
       T* dst = y + out_row(p, m) + n;
       if (n + 8 <= n_end) {
         if (whole16) {
-          *(uint4*)dst = v;
+          store16_nt(dst, v);
         } else {
           *(uint2*)dst = make_uint2(v.x, v.y);
           *(uint2*)(dst + 4) = make_uint2(v.z, v.w);

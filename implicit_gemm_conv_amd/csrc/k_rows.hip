@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void conv_rows_kernel(ConvParams p, RowsGeo
           const int o = l / ob, k = (l - o * ob) >> 4;
           const uint4 v = *(const uint4*)(ep + o * ob + ((k ^ (o & (ppo - 1))) * 16));
           const int ow = ow0 + 32 * bp + o;
-          if (oh < p.oh && ow < p.ow) *(uint4*)(yrow + (int64_t)ow * p.cout + k * 8) = v;
+          if (oh < p.oh && ow < p.ow) store16_nt(yrow + (int64_t)ow * p.cout + k * 8, v);
         }
       }
     } else if (oh < p.oh) {

@@ -33,7 +33,9 @@
 // addresses are per-lane constants plus immediates, and one 256-byte LDS pass
 // over 16 consecutive positions hits 16 distinct slots for every tap offset.
 // Fragments are double-buffered in registers; the epilogue stages the tile
-// through LDS so that stores write whole 16-byte pieces of output rows.
+// through LDS so that stores write whole 16-byte pieces of output rows, as
+// non-temporal stores (1-2% faster than ordinary ones: every workgroup writes
+// its 128 KB at the same time, at the end).
 #include <type_traits>
 
 #include "conv_device.h"
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
       T* dst = y + m * p.cout + n;
       if (n + 8 <= p.cout) {
         if (whole16) {
-          *(uint4*)dst = v;
+          store16_nt(dst, v);
         } else {
           *(uint2*)dst = make_uint2(v.x, v.y);
           *(uint2*)(dst + 4) = make_uint2(v.z, v.w);

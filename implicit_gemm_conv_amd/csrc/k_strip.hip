@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void conv_strip_kernel(ConvParams p, const 
       T* dst = y + (int64_t)m * p.cout + n;
       if (n + 8 <= p.cout) {
         if (whole16) {
-          *(uint4*)dst = v;
+          store16_nt(dst, v);
         } else {
           *(uint2*)dst = make_uint2(v.x, v.y);
           *(uint2*)(dst + 4) = make_uint2(v.z, v.w);
