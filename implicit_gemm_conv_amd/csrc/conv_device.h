@@ -93,9 +93,12 @@ __device__ __forceinline__ bool tap_valid(const RowInfo& r, int kd, int kh, int 
 // back by the kernel, and a whole grid storing its tiles at once writes
 // faster this way than through the ordinary write-allocate path (1-9% per
 // launch on the measured shapes).
+__device__ __forceinline__ void store16_nt(void* dst, u32x4_t v) {
+  __builtin_nontemporal_store(v, (u32x4_t*)dst);
+}
 __device__ __forceinline__ void store16_nt(void* dst, uint4 v) {
   const u32x4_t vv = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(vv, (u32x4_t*)dst);
+  store16_nt(dst, vv);
 }
 
 // ---- XCD-aware tile order ----

@@ -10,25 +10,26 @@
 // output's end, their extra rows computed on zeros and not stored) and 128
 // output channels.  For one (channel chunk
 // of 32, kd) the workgroup stages the 18 input rows x 34 positions that the
-// tile's windows cover (a "slab", rows padded to 36 positions, zeros outside
-// the input); output row g of the tile reads slab row g + kh for tap kh and
+// tile's windows cover (a "slab", zeros outside the input); output row g of
+// the tile reads slab row g + kh for tap kh and
 // position r + kw for tap kw, so all K_h * K_w taps of the plane come out of
 // one staging.  Per (chunk, kd) the input bytes through the caches are
-// 18 * 36 positions instead of K_h * 16 * 36.
+// 18 * 34 positions instead of K_h * 16 * 34.
 //
 // A K step is one (chunk, kd, kh); its filter slice (K_w taps x 128 output
 // channels x 32 channels) is staged per step, two stages deep.  The slab of
 // the next (chunk, kd) goes out in pieces from the MFMA blocks of the first
 // K_h - 1 steps of the current one, into the second of two slab stages, and
 // must land by the barrier that starts the next plane; the filter slice of
-// step s + 1 goes out right after the barrier that starts step s.
+// step s + 1 goes out right after the barrier that starts step s.  A slab is
+// 40 wave loads of 16 positions (612 needed), the filter slices of a step 24 KB.
 //
 // Eight waves, two per SIMD: wave v owns output rows 4 (v % 4) .. + 3 of the
 // tile (128 GEMM rows) x channels 64 (v / 4) .. + 63 = 4 x 2 blocks of
 // v_mfma_f32_32x32x16, 128 accumulator registers, so that the two waves of a
 // SIMD cover each other's barrier waits and fragment-read latency (one wave
 // per SIMD with a 128 x 128 block ran 5-9% slower on the same loads).  LDS: slab
-// position o of row r at (36 r + o) * 64 bytes, its four 16-byte channel
+// position o of row r at (34 r + o) * 64 bytes, its four 16-byte channel
 // chunks XOR-swizzled by bits 2..3 of o (the same for every row), so fragment
 // addresses are per-lane constants plus immediates, and one 256-byte LDS pass
 // over 16 consecutive positions hits 16 distinct slots for every tap offset.
@@ -53,13 +54,13 @@ constexpr int kSeg = 32;                            // outputs along w per tile 
 constexpr int kRowsOut = 16;                        // output rows along h per tile
 constexpr int kBM = kSeg * kRowsOut;                // 512 GEMM rows
 constexpr int kBN = 128;                            // output channels per tile
-constexpr int kSW = 36;                             // slab positions per row (32 + K_w - 1 <= 34)
+constexpr int kSW = 34;                             // slab positions per row (32 + K_w - 1 <= 34)
 constexpr int kMaxKW = 3;
 constexpr int kMaxKH = 3;
 constexpr int kRowsIn = kRowsOut + kMaxKH - 1;      // 18 slab rows
 constexpr int kRowB = 64;                           // bytes per position / filter row (32 channels)
-constexpr int kA_LOADS = 6;                         // 16-position wave loads per wave per slab
-constexpr int kSlabBytes = 8 * kA_LOADS * 16 * kRowB;   // 48 KB (18 x 36 positions and a spare tail)
+constexpr int kA_LOADS = 5;                         // 16-position wave loads per wave per slab
+constexpr int kSlabBytes = 8 * kA_LOADS * 16 * kRowB;   // 40 KB (18 x 34 positions and a spare tail)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kOutRowB = kBN * 2;
 constexpr int kOutTileBytes = kBM * kOutRowB;       // 128 KB
