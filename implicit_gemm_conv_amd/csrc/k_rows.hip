@@ -82,20 +82,59 @@ __global__ __launch_bounds__(256, 2) void conv_rows_kernel(ConvParams p, RowsGeo
   const int nq = g.R * g.P;               // real groups
 
   // ---- filter table: entry (q, n) = 8 halves of filter row r = q / P,
-  // run positions 8*(q % P) .. +7 (zero past the run or past C_out) ----
-  for (int e = tid; e < kMaxGroups * 64; e += 256) {
-    const int q = e >> 6, n = e & 63;
-    union { T h[8]; uint4 u; } v;
+  // run positions 8*(q % P) .. +7 (zero past the run or past C_out).  The
+  // filter (C_out * K <= 64 * 192 halves, at most lds_in's size) is first
+  // copied as it is into lds_in with consecutive threads reading consecutive
+  // elements, then the table is built from that copy: reading the table's
+  // entries straight from global memory touches one cache line per lane. ----
+  {
+    // every load issued before any LDS write: one round trip to memory
+    constexpr int kPer = kMaxGroups * 8 * 64 / 256;   // elements per thread (48)
+    static_assert(kMaxGroups * 8 * 64 * 2 <= kInBytes, "filter copy fits lds_in");
+    const int wn = p.cout * p.K;
+    T vals[kPer];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v.h[i] = (T)0.f;
-    if (q < nq && n < p.cout) {
-      const int r = q / g.P, j0 = (q % g.P) * 8;
-      const T* src = w + (int64_t)n * p.K + r * run;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (j0 + i < run) v.h[i] = src[j0 + i];
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + 256 * j;
+      vals[j] = i < wn ? w[i] : (T)0.f;
     }
-    *(uint4*)(lds_b + e * 16) = v.u;
+    T* wl = (T*)lds_in;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + 256 * j;
+      if (i < wn) wl[i] = vals[j];
+    }
+  }
+  __syncthreads();
+  {
+    // all reads issued unconditionally (addresses clamped into the copy),
+    // zeros selected afterwards: one LDS round trip instead of a branch per
+    // element
+    constexpr int kEnt = kMaxGroups * 64 / 256;   // table entries per thread (6)
+    const int wn = p.cout * p.K;
+    const T* wl = (const T*)lds_in;
+    T hv[kEnt][8];
+    bool keep[kEnt][8];
+#pragma unroll
+    for (int k = 0; k < kEnt; ++k) {
+      const int e = tid + 256 * k;
+      const int q = e >> 6, n = e & 63;
+      const bool ok = q < nq && n < p.cout;
+      const int r = ok ? q / g.P : 0, j0 = ok ? (q % g.P) * 8 : 0;
+      const int base = n * p.K + r * run + j0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hv[k][i] = wl[min(base + i, wn - 1)];
+        keep[k][i] = ok && j0 + i < run;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kEnt; ++k) {
+      union { T h[8]; uint4 u; } v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v.h[i] = keep[k][i] ? hv[k][i] : (T)0.f;
+      *(uint4*)(lds_b + (tid + 256 * k) * 16) = v.u;
+    }
   }
 
   // ---- per-lane constants ----
@@ -160,8 +199,21 @@ __global__ __launch_bounds__(256, 2) void conv_rows_kernel(ConvParams p, RowsGeo
       const int i = tid + 256 * k;
       if (i < pieces) {
         const int row = i / row_pieces, pc = i - (i / row_pieces) * row_pieces;
-        // shifted copies start 2 bytes into the row: written unaligned
-        *(uint4*)(lds_in + (row * g.row_halves + pc * 8 + g.shift) * 2) = stage_regs[k];
+        char* dst = lds_in + (row * g.row_halves + pc * 8 + g.shift) * 2;
+        const uint4 v = stage_regs[k];
+        if (g.shift == 0) {
+          *(uint4*)dst = v;
+        } else {
+          // a copy moved by one half (dst is 2 past a 16-byte boundary):
+          // halves 0 and 7 alone, the six between re-paired into an aligned
+          // dword and an aligned 8-byte pair (a misaligned 16-byte LDS write
+          // costs several times more)
+          *(uint16_t*)dst = (uint16_t)v.x;
+          *(uint32_t*)(dst + 2) = __builtin_amdgcn_alignbit(v.y, v.x, 16);
+          *(uint2*)(dst + 6) = make_uint2(__builtin_amdgcn_alignbit(v.z, v.y, 16),
+                                          __builtin_amdgcn_alignbit(v.w, v.z, 16));
+          *(uint16_t*)(dst + 14) = (uint16_t)(v.w >> 16);
+        }
       }
     }
   };
