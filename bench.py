@@ -12,7 +12,8 @@ The JSON line also carries
                 step; the slab kernel runs both unit-stride 116-GFLOP
                 convolutions) timed launch by launch with HIP events on the
                 launch stream (one before each launch, each launch timed to
-                the next event), against the MI355X dense fp16 MFMA peak;
+                the next event; timing-only events, recorded without a
+                system-scope fence), against the MI355X dense fp16 MFMA peak;
   cpu_baseline: the float64 CPU oracle on a bounded sample of the same
                 workload (a fixed set of output rows of the first convolution),
                 on this host's cores, rank 0 only.
@@ -24,6 +25,7 @@ median and min), once with resident buffers and once "cold", rotating enough
 line per workload.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -54,6 +56,54 @@ KERNELS = {
     "main": ("conv_main_kernel<fp16>: 128x128 tile, BK=64, 16x16x32 MFMA",
              ["implicit_gemm_conv_amd/csrc/k_main.hip", *_COMMON]),
 }
+
+
+class HipTimer:
+    """HIP events used only to measure time, recorded on the launch stream.
+
+    They are created with hipEventDisableSystemFence, the flag the HIP runtime
+    documents for timing-only events: recording one skips the system-scope
+    release (cache writeback and invalidation) that a default event performs,
+    which cost the stream several microseconds per event (and now and then far
+    more) and perturbed the kernel that followed.  The host reads them only
+    after torch.cuda.synchronize().  They come from the HIP runtime torch
+    loaded, so torch's stream handles are valid for them."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        lib = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.hip = ctypes.CDLL(lib if os.path.exists(lib) else "libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def event(self):
+        e = ctypes.c_void_p()
+        self._check(self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream):
+        self._check(self.hip.hipEventRecord(e, ctypes.c_void_p(stream.cuda_stream)), "hipEventRecord")
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        self._check(self.hip.hipEventElapsedTime(ctypes.byref(out), a, b), "hipEventElapsedTime")
+        return out.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
 
 
 def traffic_file(path):
@@ -147,6 +197,7 @@ def sweep(launches, names=None, tune=False):
     fastest."""
     dev = "cuda:0"
     stream = torch.cuda.current_stream()
+    timer = HipTimer()
     for name, wl in {**WORKLOADS, **VARIANT_WORKLOADS, **BWD_WORKLOADS}.items():
         if names and name not in names:
             continue
@@ -170,17 +221,18 @@ def sweep(launches, names=None, tune=False):
         ys = [y] + [torch.empty_like(y) for _ in range(sets - 1)]
 
         def timed(pairs):
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in pairs]
+            evs = [(timer.event(), timer.event()) for _ in pairs]
             for (xi, yi), (a, b) in zip(pairs, evs):
-                a.record(stream)
+                timer.record(a, stream)
                 if bwd:
                     igc.conv_bwd_data(xi, w, wl.dx_shape, wl.stride, wl.padding, out=yi, wt=wt)
                 else:
                     igc.conv_fwd(xi, w, wl.stride, wl.padding, out=yi, **_var(wl))
-                b.record(stream)
+                timer.record(b, stream)
             torch.cuda.synchronize()
-            return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+            t = np.array([timer.ms(a, b) * 1e3 for a, b in evs])
+            timer.close()
+            return t
 
         timed([(x, y)] * 10)
         warm = timed([(x, y)] * launches)
@@ -246,7 +298,7 @@ def main():
         for i, wl in enumerate(wls):
             x, w = inputs[i]
             if marks is not None:
-                marks[i].record(stream)
+                timer.record(marks[i], stream)
             igc.conv_fwd(x, w, wl.stride, wl.padding, out=outs[i])
 
     for _ in range(args.warmup):
@@ -257,21 +309,22 @@ def main():
     # event goes on the launch stream before every launch (and one after the
     # last), so each launch is timed from its own event to the next one: one
     # event per launch instead of a pair (each event costs the stream a few us).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in wls] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    timer = HipTimer()
+    ev = [[timer.event() for _ in wls] for _ in range(args.steps)]
+    t_start = timer.event()
+    t_end = timer.event()
     torch.cuda.synchronize()
-    t_start.record(stream)
+    timer.record(t_start, stream)
     for s in range(args.steps):
         step(ev[s])
-    t_end.record(stream)
+    timer.record(t_end, stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    total_ms = timer.ms(t_start, t_end)
     ms_per_step = total_ms / args.steps
 
     def launch_ms(s, i):
         nxt = ev[s][i + 1] if i + 1 < len(wls) else (ev[s + 1][0] if s + 1 < args.steps else t_end)
-        return ev[s][i].elapsed_time(nxt)
+        return timer.ms(ev[s][i], nxt)
 
     per = {}
     for i, wl in enumerate(wls):
@@ -288,6 +341,7 @@ def main():
     dom_path = max(share, key=share.get)
     dom = [i for i, k in enumerate(keys) if k == dom_path]
     dom_us = float(np.mean([1e3 * launch_ms(s, i) for s in range(args.steps) for i in dom]))
+    timer.close()
     dom_flops = float(np.mean([flops[i] for i in dom]))
     achieved = dom_flops / (dom_us * 1e-6) / 1e12
     alg_bytes = [2 * (int(np.prod(wl.x_shape)) + int(np.prod(wl.w_shape)) +
