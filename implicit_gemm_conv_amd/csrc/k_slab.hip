@@ -8,12 +8,11 @@
 // output rows along h times 32 consecutive outputs along w (512 GEMM rows, one
 // depth plane of one image; the last tiles along h and w may hang over the
 // output's end, their extra rows computed on zeros and not stored) and 128
-// output channels.  For one (channel chunk
-// of 32, kd) the workgroup stages the 18 input rows x 34 positions that the
-// tile's windows cover (a "slab", zeros outside the input); output row g of
-// the tile reads slab row g + kh for tap kh and
-// position r + kw for tap kw, so all K_h * K_w taps of the plane come out of
-// one staging.  Per (chunk, kd) the input bytes through the caches are
+// output channels.  For one (channel chunk of 32, kd) the workgroup stages the
+// 18 input rows x 34 positions that the tile's windows cover (a "slab", zeros
+// outside the input); output row g of the tile reads slab row g + kh for tap
+// kh and position r + kw for tap kw, so all K_h * K_w taps of the plane come
+// out of one staging.  Per (chunk, kd) the input bytes through the caches are
 // 18 * 34 positions instead of K_h * 16 * 34.
 //
 // A K step is one (chunk, kd, kh); its filter slice (K_w taps x 128 output
