@@ -350,6 +350,7 @@ hipError_t launch_variant(int v, const ConvParams& p, const void* x, const void*
     case 47: return launch_cfg<T, 128, 128, 64, 2, 2, 3, 1, 32>(p, x, w, y, s);
     case 48: return launch_cfg<T, 128, 128, 32, 2, 2, 3, 2, 32>(p, x, w, y, s);
     case 49: return launch_cfg<T, 128, 64, 32, 2, 2, 3, 2, 32>(p, x, w, y, s);
+    case 50: return launch_cfg<T, 128, 128, 32, 2, 2, 2, 3, 32>(p, x, w, y, s);
     default: return launch_cfg<T, 128, 64, 32, 2, 2, 3, 2, 16>(p, x, w, y, s);
   }
 }
@@ -362,6 +363,12 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
 #endif
   const bool bk64 = p.cin_g % 64 == 0;
   const long tiles_256 = (long)((p.M + 255) / 256) * p.groups * ((p.cout_g + 127) / 128);
+  const long tiles_128 = (long)((p.M + 127) / 128) * p.groups * ((p.cout_g + 127) / 128);
+  // A short GEMM depth (a few K steps per tile: 3x1x1 or 1x1 filters) leaves
+  // each tile's first loads and last stores exposed; 128x128 tiles with BK = 32
+  // and 32x32x16 MFMAs fit three workgroups per CU, which overlap more of them
+  // (3x1x1 (4,32^3,64->128): 17 us against 21 us on the 128x128, BK = 64 tile).
+  if (p.K <= 192 && p.cout_g > 64 && tiles_128 >= 512) return launch_variant<T>(50, p, x, w, y, s);
   // groups of at most 64 output channels: a 64-wide column tile (a 128-wide one
   // would leave half its columns idle)
   if (p.cout_g <= 64 && bk64 && tiles_256 >= 256) return launch_variant<T>(14, p, x, w, y, s);
@@ -383,7 +390,7 @@ hipError_t launch_main(const ConvParams& p, int dtype, const void* x, const void
 }
 
 const int* main_tile_configs(int* count) {
-  static const int kConfigs[] = {9, 14, 4, 3, 8, 13, 11, 10, 7, 12, 1, 43, 47, 49};
+  static const int kConfigs[] = {9, 14, 4, 3, 8, 13, 11, 10, 7, 12, 1, 43, 47, 49, 50};
   *count = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
   return kConfigs;
 }

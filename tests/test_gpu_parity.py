@@ -136,6 +136,21 @@ def test_parity_full_size_sampled(name):
     assert torch.isfinite(y.float()).all()
 
 
+@pytest.mark.parametrize("xs,ws,st,pd", [
+    ((1, 17, 61, 64, 64), (132, 3, 1, 1, 64), (1, 1, 1), (1, 0, 0)),   # K = 192, ragged M and N tiles
+    ((2, 130, 260, 96), (256, 1, 1, 96), (1, 1), (0, 0)),               # 1x1, K = 96
+], ids=["3x1x1_c132_ragged", "1x1_2d_c256"])
+def test_main_short_depth_tiles(xs, ws, st, pd):
+    """Problems with a short GEMM depth and at least 512 tiles of 128x128 take the main path's
+    short-depth tile (BK = 32, 32x32x16, three workgroups per CU); checked on every output."""
+    wl = _case("short_k", "bf16", xs, ws, st, pd, seed=31)
+    assert igc.select_path(xs, ws, st, pd, torch.bfloat16) == "main"
+    print(f"[short-k] {xs} {ws}", flush=True)
+    x, w, y = _run(wl)
+    ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), st, pd)
+    assert_parity(oracle.to_float64(y), ref, "bf16", f"short-k {xs}")
+
+
 # ---- bit-exact index and boundary handling ----------------------------------------
 
 EXACT = [
