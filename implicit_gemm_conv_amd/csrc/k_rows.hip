@@ -88,21 +88,33 @@ __global__ __launch_bounds__(256, 2) void conv_rows_kernel(ConvParams p, RowsGeo
   // elements, then the table is built from that copy: reading the table's
   // entries straight from global memory touches one cache line per lane. ----
   {
-    // every load issued before any LDS write: one round trip to memory
-    constexpr int kPer = kMaxGroups * 8 * 64 / 256;   // elements per thread (48)
-    static_assert(kMaxGroups * 8 * 64 * 2 <= kInBytes, "filter copy fits lds_in");
+    // 16-byte pieces (the hardware serves unaligned buffer loads at any
+    // alignment), all six per thread in flight before any LDS write: 2-byte
+    // loads took 48 instructions per thread, with every workgroup reading the
+    // same lines at once at the start
+    constexpr int kPieces = kMaxGroups * 8 * 64 / 8 / 256;   // 16-byte pieces per thread (6)
+    static_assert(kPieces * 256 * 16 <= kInBytes, "filter copy fits lds_in");
     const int wn = p.cout * p.K;
-    T vals[kPer];
+    const int wbytes = wn * 2;
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, wbytes, kRawBufferFlags);
+    u32x4_t pcs[kPieces];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = tid + 256 * j;
-      vals[j] = i < wn ? w[i] : (T)0.f;
+    for (int j = 0; j < kPieces; ++j) {
+      const int k = tid + 256 * j;
+      pcs[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, k * 16 < wbytes ? (uint32_t)(k * 16) : kOutOfRange, 0, 0);
     }
-    T* wl = (T*)lds_in;
+    // with an odd element count the last element shares a dword with what
+    // lies past the filter, which the range check drops: its piece's owner
+    // copies it on its own after writing the piece
+    const int k_last = (wbytes - 2) / 16;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = tid + 256 * j;
-      if (i < wn) wl[i] = vals[j];
+    for (int j = 0; j < kPieces; ++j) {
+      const int k = tid + 256 * j;
+      if (k * 16 < wbytes) {
+        *(u32x4_t*)(lds_in + k * 16) = pcs[j];
+        if (k == k_last && (wn & 1)) ((T*)lds_in)[wn - 1] = w[wn - 1];
+      }
     }
   }
   __syncthreads();

@@ -60,6 +60,8 @@ CASES = [
           seed=27),
     _case("slab_fp16_2d_w56_ragged", "fp16", (2, 12, 56, 64), (64, 3, 3, 64), (1, 1), (1, 1), seed=28),
     _case("slab_bf16_w9_narrow", "bf16", (1, 3, 5, 9, 32), (40, 2, 2, 3, 32), (1, 1, 1), (0, 0, 1), seed=29),
+    # an odd filter element count (7 x 27): the rows path copies its filter in 16-byte pieces
+    _case("rows_odd_filter_fp16", "fp16", (1, 9, 16, 3), (7, 3, 3, 3), (1, 1), (1, 1), seed=30),
 ]
 PATHS = ["slab", "strip", "main", "brick", "rows", "runs", "flatk", "direct"]
 
