@@ -63,10 +63,10 @@ template <> __device__ __forceinline__ float slice_elem<__bf16>(const u4& v, int
 
 // Outputs along w per thread of the tiled kernel: as many as fit in the
 // register budget of its occupancy (accumulators, the window row's loads and
-// one tap's weights).
-template <int CG, int KW, int SW>
+// one tap's weights); with two output rows per thread (TH = 2) four.
+template <int CG, int KW, int SW, int TH>
 constexpr int tiled_tw() {
-  return (CG <= 2 && KW * SW <= 3) ? 8 : (CG <= 4 ? 4 : 2);
+  return TH == 2 ? 4 : (CG <= 2 && KW * SW <= 3) ? 8 : (CG <= 4 ? 4 : 2);
 }
 
 // Workgroups per CU the tiled kernel is built for: depthwise slices keep 8
@@ -74,9 +74,9 @@ constexpr int tiled_tw() {
 // spill at four workgroups per CU (128 registers) but fit at three (170);
 // three runs depthwise 3x3x3 16% faster, while the narrower groups are 8%
 // faster at four.
-template <int CG>
+template <int CG, int TH>
 constexpr int tiled_occ() {
-  return CG == 1 ? 3 : 4;
+  return CG == 1 ? 3 : 4;   // (TH = 2, depthwise only, holds 2 x 4 x 8 accumulators)
 }
 
 // Dot products of pairs of channels (v_dot2_f32_{f16,bf16}: two products
@@ -99,15 +99,16 @@ template <typename T, int CG>
 constexpr bool use_dot2() { return sizeof(T) == 2 && CG >= 2; }
 
 // ---- tiled kernel: C_out/G == C_in/G = CG, 16-byte slices, K_w = KW, stride SW ----
-// Persistent: the grid is at most what the chip holds at four waves per
-// SIMD, and each thread strides over (slice, run of TW outputs) units.
-template <typename T, int CG, int KW, int SW>
-__global__ __launch_bounds__(256, tiled_occ<CG>()) void conv_grouped_tiled_kernel(ConvParams p, const T* __restrict__ x,
-                                                                    const T* __restrict__ w,
-                                                                    T* __restrict__ y, int tiles_w) {
+// Persistent: the grid is at most what the chip holds at the kernel's
+// occupancy, and each thread strides over (slice, TH output rows x TW outputs)
+// units.
+template <typename T, int CG, int KW, int SW, int TH>
+__global__ __launch_bounds__(256, (tiled_occ<CG, TH>())) void conv_grouped_tiled_kernel(
+    ConvParams p, const T* __restrict__ x, const T* __restrict__ w, T* __restrict__ y, int tiles_w) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int VE = 16 / (int)sizeof(T);      // channels per slice
-  constexpr int TW = tiled_tw<CG, KW, SW>();   // outputs along w per unit
+  constexpr int TW = tiled_tw<CG, KW, SW, TH>();   // outputs along w per unit
+  static_assert(TH == 1 || TH == 2, "output rows per unit");
   constexpr int NP = (TW - 1) * SW + KW;       // input positions per window row
   constexpr bool D2 = use_dot2<T, CG>();
   // one tap's weights for a slice: VE * CG values, as fp32 or as channel pairs
@@ -134,7 +135,8 @@ __global__ __launch_bounds__(256, tiled_occ<CG>()) void conv_grouped_tiled_kerne
 
   // Unit counts stay below 2^31: x and y are below 2^31 bytes.
   const int U = p.cin / VE;                    // slices per position
-  const int units = p.n * p.od * p.oh * tiles_w * U;
+  const int ohu = (p.oh + TH - 1) / TH;       // units along h
+  const int units = p.n * p.od * ohu * tiles_w * U;
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)x, (short)0, (int)((int64_t)p.n * p.xs_n * (int)sizeof(T)), kRawBufferFlags);
 
@@ -143,23 +145,28 @@ __global__ __launch_bounds__(256, tiled_occ<CG>()) void conv_grouped_tiled_kerne
     int r = idx / U;
     const int twi = r % tiles_w;
     r /= tiles_w;
-    const int yo = r % p.oh;
-    r /= p.oh;
+    const int yo = (r % ohu) * TH;              // first output row of the unit
+    r /= ohu;
     const int zo = r % p.od;
     const int n = r / p.od;
     const int ow0 = twi * TW;
     const int xi0 = ow0 * SW - p.pw;
 
-    float acc[TW][VE];
+    float acc[TH][TW][VE];
 #pragma unroll
-    for (int t = 0; t < TW; ++t)
+    for (int h = 0; h < TH; ++h)
 #pragma unroll
-      for (int j = 0; j < VE; ++j) acc[t][j] = 0.f;
+      for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int j = 0; j < VE; ++j) acc[h][t][j] = 0.f;
 
     for (int a = 0; a < p.kd; ++a) {
       const int zi = zo * p.sd - p.pd + a * p.ed;
       if (zi < 0 || zi >= p.d) continue;
-      for (int b = 0; b < p.kh; ++b) {
+      // TH = 1: input row b of the window (any stride and dilation along h).
+      // TH = 2 (unit stride, undilated): input row b serves output row h with
+      // tap b - h, so each of the K_h + 1 rows is loaded once for both.
+      for (int b = 0; b < p.kh + TH - 1; ++b) {
         const int yi = yo * p.sh - p.ph + b * p.eh;
         if (yi < 0 || yi >= p.h) continue;
         const int row = n * p.xs_n + zi * p.xs_d + yi * p.xs_h + u * VE;
@@ -171,8 +178,12 @@ __global__ __launch_bounds__(256, tiled_occ<CG>()) void conv_grouped_tiled_kerne
           xv[j] = __builtin_amdgcn_raw_buffer_load_b128(
               xr, ok ? (uint32_t)((row + xi * p.xs_w) * (int)sizeof(T)) : kOutOfRange, 0, 0);
         }
-        // this slice's weights of tap (a, b, 0), in dwords
-        const uint32_t* wrow = wls + ((a * p.kh + b) * KW * p.cout + u * VE) * CG / (D2 ? 2 : 1);
+#pragma unroll
+        for (int h = 0; h < TH; ++h) {
+        const int tb = b - h;                    // the tap this row is for output row h
+        if (tb < 0 || tb >= p.kh) continue;
+        // this slice's weights of tap (a, tb, 0), in dwords
+        const uint32_t* wrow = wls + ((a * p.kh + tb) * KW * p.cout + u * VE) * CG / (D2 ? 2 : 1);
 #pragma unroll
         for (int e = 0; e < KW; ++e) {
           uint32_t wv[NWD];
@@ -190,8 +201,8 @@ __global__ __launch_bounds__(256, tiled_occ<CG>()) void conv_grouped_tiled_kerne
               for (int t = 0; t < TW; ++t)
 #pragma unroll
                 for (int o = 0; o < VE; ++o)
-                  acc[t][o] = dot2(xv[t * SW + e][(o / CG) * (CG / 2) + c2], wv[o * (CG / 2) + c2],
-                                   acc[t][o], (T*)nullptr);
+                  acc[h][t][o] = dot2(xv[t * SW + e][(o / CG) * (CG / 2) + c2], wv[o * (CG / 2) + c2],
+                                      acc[h][t][o], (T*)nullptr);
           } else {
             // channel outermost: consecutive FMAs update different accumulators
 #pragma unroll
@@ -200,21 +211,26 @@ __global__ __launch_bounds__(256, tiled_occ<CG>()) void conv_grouped_tiled_kerne
               for (int t = 0; t < TW; ++t)
 #pragma unroll
                 for (int o = 0; o < VE; ++o)   // (o / CG) * CG is the first channel of o's group
-                  acc[t][o] = fmaf(slice_elem<T>(xv[t * SW + e], (o / CG) * CG + c),
-                                   __builtin_bit_cast(float, wv[o * CG + c]), acc[t][o]);
+                  acc[h][t][o] = fmaf(slice_elem<T>(xv[t * SW + e], (o / CG) * CG + c),
+                                      __builtin_bit_cast(float, wv[o * CG + c]), acc[h][t][o]);
           }
+        }
         }
       }
     }
 
-    T* yrow = y + ((((int64_t)n * p.od + zo) * p.oh + yo) * p.ow) * p.cout + u * VE;
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      if (ow0 + t < p.ow) {
-        T out[VE];
+    for (int h = 0; h < TH; ++h) {
+      if (yo + h >= p.oh) continue;
+      T* yrow = y + ((((int64_t)n * p.od + zo) * p.oh + yo + h) * p.ow) * p.cout + u * VE;
 #pragma unroll
-        for (int j = 0; j < VE; ++j) out[j] = from_f32<T>(acc[t][j]);
-        store16_nt(yrow + (int64_t)(ow0 + t) * p.cout, __builtin_bit_cast(u32x4_t, out));
+      for (int t = 0; t < TW; ++t) {
+        if (ow0 + t < p.ow) {
+          T out[VE];
+#pragma unroll
+          for (int j = 0; j < VE; ++j) out[j] = from_f32<T>(acc[h][t][j]);
+          store16_nt(yrow + (int64_t)(ow0 + t) * p.cout, __builtin_bit_cast(u32x4_t, out));
+        }
       }
     }
   }
@@ -304,20 +320,30 @@ int device_cus() {
   return v;
 }
 
-template <typename T, int CG, int KW, int SW>
-hipError_t launch_tiled_sw(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
+template <typename T, int CG, int KW, int SW, int TH>
+hipError_t launch_tiled_th(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   constexpr int VE = 16 / (int)sizeof(T);
-  constexpr int TW = tiled_tw<CG, KW, SW>();
+  constexpr int TW = tiled_tw<CG, KW, SW, TH>();
   const int tiles_w = (p.ow + TW - 1) / TW;
-  const int64_t units = (int64_t)p.n * p.od * p.oh * tiles_w * (p.cin / VE);
+  const int64_t units = (int64_t)p.n * p.od * ((p.oh + TH - 1) / TH) * tiles_w * (p.cin / VE);
   int64_t blocks = (units + 255) / 256;
   // persistent: as many workgroups as the chip holds at the kernel's occupancy
-  const int cap = tiled_occ<CG>() * device_cus();
+  const int cap = tiled_occ<CG, TH>() * device_cus();
   if (blocks > cap) blocks = cap;
   const size_t lds = (size_t)p.cout * p.K * (use_dot2<T, CG>() ? sizeof(T) : sizeof(float));
-  hipLaunchKernelGGL((conv_grouped_tiled_kernel<T, CG, KW, SW>), dim3((unsigned)blocks), dim3(256), lds, s,
+  hipLaunchKernelGGL((conv_grouped_tiled_kernel<T, CG, KW, SW, TH>), dim3((unsigned)blocks), dim3(256), lds, s,
                      p, (const T*)x, (const T*)w, (T*)y, tiles_w);
   return hipGetLastError();
+}
+
+// Depthwise at unit stride and no dilation along h, filters up to 3 wide: two
+// output rows per thread, each input row loaded once for both.
+template <typename T, int CG, int KW, int SW>
+hipError_t launch_tiled_sw(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
+  if constexpr (CG == 1 && SW == 1 && KW <= 3) {
+    if (p.sh == 1 && p.eh == 1) return launch_tiled_th<T, CG, KW, SW, 2>(p, x, w, y, s);
+  }
+  return launch_tiled_th<T, CG, KW, SW, 1>(p, x, w, y, s);
 }
 
 template <typename T, int CG, int KW>

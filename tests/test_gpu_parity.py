@@ -306,6 +306,8 @@ VARIANTS = [
      ((4, 4), (2, 2)), (2, 1), 40),
     ("depthwise3d_fp32_k3_ragged", "fp32", (2, 6, 7, 37, 12), (12, 3, 3, 3, 1), (2, 1, 1),
      ((1, 1), (1, 1), (1, 1)), (1, 1, 1), 12),
+    ("depthwise2d_fp16_k3_odd_h", "fp16", (2, 15, 21, 32), (32, 3, 3, 1), (1, 1),
+     ((1, 1), (1, 1)), (1, 1), 32),
     ("depthwise2d_fp16_k7_c64", "fp16", (2, 20, 35, 64), (64, 7, 7, 1), (1, 1),
      ((3, 3), (3, 3)), (1, 1), 64),
 ]
