@@ -52,7 +52,6 @@ constexpr int kRawBufferFlags = 0x00020000;
 constexpr int kSeg = 32;                            // outputs along w per tile row
 constexpr int kRowsOut = 16;                        // output rows along h per tile
 constexpr int kBM = kSeg * kRowsOut;                // 512 GEMM rows
-constexpr int kBN = 128;                            // output channels per tile
 constexpr int kSW = 34;                             // slab positions per row (32 + K_w - 1 <= 34)
 constexpr int kMaxKW = 3;
 constexpr int kMaxKH = 3;
@@ -61,8 +60,6 @@ constexpr int kRowB = 64;                           // bytes per position / filt
 constexpr int kA_LOADS = 5;                         // 16-position wave loads per wave per slab
 constexpr int kSlabBytes = 8 * kA_LOADS * 16 * kRowB;   // 40 KB (18 x 34 positions and a spare tail)
 constexpr int kLdsBytes = 160 * 1024;
-constexpr int kOutRowB = kBN * 2;
-constexpr int kOutTileBytes = kBM * kOutRowB;       // 128 KB
 static_assert(8 * kA_LOADS * 16 >= kRowsIn * kSW, "slab loads cover the slab");
 
 template <int N>
@@ -84,29 +81,43 @@ __device__ __forceinline__ void static_for(F&& f) {
 // physical 16-byte chunk of logical chunk c at slab position o (or filter row o)
 __device__ __forceinline__ int swz(int o, int c) { return c ^ ((o >> 2) & 3); }
 
-template <typename T, int KW, int KH>
+template <typename T, int KW, int KH, int NB>
 __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T* __restrict__ x,
                                                            const T* __restrict__ w,
                                                            T* __restrict__ y, int tiles_n,
                                                            uint32_t x_bytes, uint32_t w_bytes) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef typename Vec8<T>::type V8;
-  constexpr int B_ROWS = KW * kBN;                 // filter rows per step
+  static_assert(NB == 128 || NB == 64, "channels per tile");
+  constexpr int WR = NB == 128 ? 4 : 2;            // output rows (A fragments) per wave
+  constexpr int NM = 2 * WR;                       // MFMAs per block per wave
+  constexpr int B_ROWS = KW * NB;                  // filter rows per step
   constexpr int B_BYTES = B_ROWS * kRowB;
-  constexpr int B_LOADS = B_ROWS * 4 / 512;        // 16-byte pieces per thread
+  constexpr int B_PIECES = B_ROWS * 4;             // 16-byte pieces per step (a multiple of 64)
+  constexpr int B_LOADS = (B_PIECES + 511) / 512;  // per thread (the last round: the first waves)
   static_assert(KW >= 1 && KW <= kMaxKW && KH >= 2 && KH <= kMaxKH, "filter extents");
+  static_assert(B_PIECES % 64 == 0, "whole waves of filter pieces");
   constexpr int B_BASE = 2 * kSlabBytes;
   constexpr int RING = B_BASE + 2 * B_BYTES;
   static_assert(RING <= kLdsBytes, "LDS");
-  constexpr int SMEM = RING > kOutTileBytes ? RING : kOutTileBytes;
+  constexpr int OUT_ROWB = NB * 2;                 // one output row of the tile in LDS
+  constexpr int OCH = NB / 8;                      // its 16-byte pieces
+  constexpr int OUT_TILE = kBM * OUT_ROWB;
+  constexpr int SMEM = RING > OUT_TILE ? RING : OUT_TILE;
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 3, wn = wave >> 2;
+  // NB = 128: wave v owns output rows 4 (v % 4) .. + 3, channels 64 (v / 4) ..;
+  // NB = 64: output rows 2 v .. 2 v + 1, all 64 channels
+  const int wm = NB == 128 ? (wave & 3) : wave, wn = NB == 128 ? (wave >> 2) : 0;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int n0 = (tile % tiles_n) * kBN;
+  const int n0 = (tile % tiles_n) * NB;
+  // a column tile never straddles a channel group (NB divides C_out/G when
+  // G > 1): the group's input channels start at cbase, its outputs end at n_end
+  const int grp = n0 / p.cout_g;
+  const int cbase = grp * p.cin_g, n_end = (grp + 1) * p.cout_g;
   // tile rows: w-block fastest, then h-block, depth, image
   const int wblocks = (p.ow + kSeg - 1) / kSeg, hblocks = (p.oh + kRowsOut - 1) / kRowsOut;
   int t = tile / tiles_n;
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
     uint32_t base = 0, mask = 0;
     if (r < kRowsOut + KH - 1 && o < kSeg + KW - 1 && ih >= 0 && ih < p.h && iw >= 0 && iw < p.w) {
       mask = dmask;
-      base = (uint32_t)(((img * p.xs_n + z0 * p.xs_d + ih * p.xs_h + iw * p.xs_w) + c * 8) * 2);
+      base = (uint32_t)(((img * p.xs_n + z0 * p.xs_d + ih * p.xs_h + iw * p.xs_w) + cbase + c * 8) * 2);
     }
     a_base[q] = base;
     a_mask[q] = mask;
@@ -151,14 +162,14 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
 #pragma unroll
   for (int s = 0; s < B_LOADS; ++s) {
     const int j = s * 512 + tid;
-    const int row = j >> 2, phys = j & 3;     // row = kw * 128 + n
-    const int kw = row / kBN, n = row % kBN;
+    const int row = j >> 2, phys = j & 3;     // row = kw * NB + n
+    const int kw = row / NB, n = row % NB;
     const int c = swz(row, phys);
-    b_base[s] = (n0 + n) < p.cout ? (uint32_t)(((n0 + n) * p.K + kw * p.cin + c * 8) * 2)
-                                  : kOutOfRange;
+    b_base[s] = j < B_PIECES && (n0 + n) < n_end ? (uint32_t)(((n0 + n) * p.K + kw * p.cin_g + c * 8) * 2)
+                                                 : kOutOfRange;
   }
 
-  const int nchunks = p.cin / 32;
+  const int nchunks = p.cin_g / 32;
   const int NG = nchunks * p.kd;               // slabs: (chunk, kd), kd fastest
   // Past the last slab or step every load zero-fills (masks, not branches),
   // into a stage no step reads any more.
@@ -186,12 +197,16 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
   auto issue_b = [&]() __attribute__((always_inline)) {
     char* sb = smem + B_BASE + b_slot * B_BYTES;
     const uint32_t live = b_ic < nchunks ? ~0u : 0u;
-    const uint32_t woff = (uint32_t)(((b_kd * KH + b_kh) * KW * p.cin + b_ic * 32) * 2);
+    const uint32_t woff = (uint32_t)(((b_kd * KH + b_kh) * KW * p.cin_g + b_ic * 32) * 2);
 #pragma unroll
     for (int s = 0; s < B_LOADS; ++s)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wr, (lds_ptr_t)(sb + (s * 512 + wave * 64) * 16), 16, (b_base[s] + woff) | (~live & kOutOfRange), 0,
-          0, 0);
+      // every wave loads in all but a partial last round (64-channel tiles:
+      // there only the first waves, wave-uniformly); a compile-time "yes"
+      // elsewhere keeps branches out of the MFMA-interleaved code
+      if ((s + 1 < B_LOADS || B_PIECES % 512 == 0) || s * 512 + wave * 64 < B_PIECES)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (lds_ptr_t)(sb + (s * 512 + wave * 64) * 16), 16, (b_base[s] + woff) | (~live & kOutOfRange),
+            0, 0, 0);
     const int h1 = b_kh + 1;
     const bool wh = h1 == KH;
     b_kh = wh ? 0 : h1;
@@ -203,7 +218,7 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
   };
 
   // ---- fragment addresses: lane (r = lane % 32, g2 = lane / 32); tile row
-  // 4 wm + a reads slab row 4 wm + a + kh ----
+  // WR wm + a reads slab row WR wm + a + kh ----
   const int r = lane & 31, g2 = lane >> 5;
   int a_addr[KW][2], b_addr[2];
 #pragma unroll
@@ -211,14 +226,14 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int o = r + kw;
-      a_addr[kw][ks] = (wm * 4 * kSW + o) * kRowB + swz(o, 2 * ks + g2) * 16;
+      a_addr[kw][ks] = (wm * WR * kSW + o) * kRowB + swz(o, 2 * ks + g2) * 16;
     }
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) b_addr[ks] = r * kRowB + swz(r, 2 * ks + g2) * 16;
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[WR][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < WR; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -229,17 +244,17 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
   // passes the barrier first and reads the next step's first fragments.
   constexpr int NBLK = 2 * KW;
   constexpr int USLOTS = (KH - 1) * (NBLK - 1);   // blocks that carry slab pieces
-  V8 fa[2][4], fb[2][2];
-  auto read_block = [&](V8(&af)[4], V8(&bf)[2], const char* sa, const char* sb, int kw, int ks)
+  V8 fa[2][WR], fb[2][2];
+  auto read_block = [&](V8(&af)[WR], V8(&bf)[2], const char* sa, const char* sb, int kw, int ks)
       __attribute__((always_inline)) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) af[a] = *(const V8*)(sa + a_addr[kw][ks] + a * kSW * kRowB);
+    for (int a = 0; a < WR; ++a) af[a] = *(const V8*)(sa + a_addr[kw][ks] + a * kSW * kRowB);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) bf[b] = *(const V8*)(sb + b_addr[ks] + (kw * kBN + wn * 64 + b * 32) * kRowB);
+    for (int b = 0; b < 2; ++b) bf[b] = *(const V8*)(sb + b_addr[ks] + (kw * NB + wn * 64 + b * 32) * kRowB);
   };
-  auto mma_block = [&](const V8(&af)[4], const V8(&bf)[2]) __attribute__((always_inline)) {
+  auto mma_block = [&](const V8(&af)[WR], const V8(&bf)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < WR; ++a)
 #pragma unroll
       for (int b = 0; b < 2; ++b) acc[a][b] = mfma32x32x16(bf[b], af[a], acc[a][b]);
   };
@@ -264,11 +279,11 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
           issue_a_part((u * kA_LOADS) / USLOTS, ((u + 1) * kA_LOADS) / USLOTS);
         }
         mma_block(fa[cur], fb[cur]);
-        // in the shadow of each MFMA: a fragment read (first 6), address VALU, a load
+        // in the shadow of each MFMA: a fragment read (the first WR + 2), address VALU, a load
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NM; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (i < WR + 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
@@ -281,11 +296,11 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
         issue_b();                          // the step after next, into this step's filter stage
         mma_block(fa[cur], fb[cur]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NM; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if (i < WR + 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, (B_LOADS + 7) / 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, (B_LOADS + NM - 1) / NM, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       } else {
@@ -325,45 +340,45 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
 
   // ---- epilogue: the tile goes through LDS so each store writes whole
   // 16-byte pieces of output rows.  Lane (r, g2) holds tile rows
-  // 32 (4 wm + a) + r and channels 64 wn + 32 b + 8 q + 4 g2 + i; in LDS a row
-  // is 256 bytes, its 16-byte piece k at slot k ^ (row % 16); after a barrier
-  // the workgroup stores the whole tile.  Wait for the zero-fill loads
+  // 32 (WR wm + a) + r and channels 64 wn + 32 b + 8 q + 4 g2 + i; in LDS a row
+  // is NB * 2 bytes, its 16-byte piece k at slot k ^ (row % OCH); after a
+  // barrier the workgroup stores the whole tile.  Wait for the zero-fill loads
   // past the end and for every wave's last reads first. ----
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < WR; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int row = (wm * 4 + a) * 32 + r;
+        const int row = (wm * WR + a) * 32 + r;
         const int k = wn * 8 + 4 * b + q;
         union { T h[4]; uint2 u; } pk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[a][b][4 * q + i]);
-        *(uint2*)(smem + row * kOutRowB + ((k ^ (row & 15)) * 16) + g2 * 8) = pk.u;
+        *(uint2*)(smem + row * OUT_ROWB + ((k ^ (row & (OCH - 1))) * 16) + g2 * 8) = pk.u;
       }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const bool whole16 = (p.cout & 7) == 0;   // 16-byte stores stay aligned
   const int64_t plane = (int64_t)(img * p.od + od) * p.oh;
 #pragma unroll 4
-  for (int i = 0; i < kBM * 16 / 512; ++i) {
+  for (int i = 0; i < kBM * OCH / 512; ++i) {
     const int piece = i * 512 + tid;
-    const int row = piece >> 4, k = piece & 15;
-    const uint4 v = *(const uint4*)(smem + row * kOutRowB + ((k ^ (row & 15)) * 16));
+    const int row = piece / OCH, k = piece % OCH;
+    const uint4 v = *(const uint4*)(smem + row * OUT_ROWB + ((k ^ (row & (OCH - 1))) * 16));
     const int oh = oh0 + (row >> 5);
     const int n = n0 + k * 8;
     if (oh < p.oh && ow0 + (row & 31) < p.ow) {
       const int64_t m = (plane + oh) * p.ow + ow0 + (row & 31);
       T* dst = y + m * p.cout + n;
-      if (n + 8 <= p.cout) {
+      if (n + 8 <= n_end) {
         if (whole16) {
           store16_nt(dst, v);
         } else {
           *(uint2*)dst = make_uint2(v.x, v.y);
           *(uint2*)(dst + 4) = make_uint2(v.z, v.w);
         }
-      } else if (n + 4 <= p.cout) {
+      } else if (n + 4 <= n_end) {
         *(uint2*)dst = make_uint2(v.x, v.y);
       }
     }
@@ -371,23 +386,31 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <typename T, int KW, int KH>
+template <typename T, int KW, int KH, int NB>
 hipError_t launch_k(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   const int tiles_m = p.n * p.od * ((p.oh + kRowsOut - 1) / kRowsOut) * ((p.ow + kSeg - 1) / kSeg);
-  const int tiles_n = (p.cout + kBN - 1) / kBN;
+  const int tiles_n = (p.cout + NB - 1) / NB;
   const uint32_t xb = (uint32_t)((int64_t)p.n * p.xs_n * 2);
   const uint32_t wb = (uint32_t)((int64_t)p.cout * p.K * 2);
-  hipLaunchKernelGGL((conv_slab_kernel<T, KW, KH>), dim3(tiles_m * tiles_n), dim3(512), 0, s, p,
+  hipLaunchKernelGGL((conv_slab_kernel<T, KW, KH, NB>), dim3(tiles_m * tiles_n), dim3(512), 0, s, p,
                      (const T*)x, (const T*)w, (T*)y, tiles_n, xb, wb);
   return hipGetLastError();
+}
+
+// 64-channel tiles for grouped layers (a tile stays inside one group) and for
+// C_out <= 64 (a 128-channel tile would leave half its columns idle).
+template <typename T, int KW, int KH>
+hipError_t launch_nb(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
+  if (p.groups > 1 || p.cout <= 64) return launch_k<T, KW, KH, 64>(p, x, w, y, s);
+  return launch_k<T, KW, KH, 128>(p, x, w, y, s);
 }
 
 template <typename T, int KH>
 hipError_t launch_kh(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   switch (p.kw) {
-    case 1: return launch_k<T, 1, KH>(p, x, w, y, s);
-    case 2: return launch_k<T, 2, KH>(p, x, w, y, s);
-    default: return launch_k<T, 3, KH>(p, x, w, y, s);
+    case 1: return launch_nb<T, 1, KH>(p, x, w, y, s);
+    case 2: return launch_nb<T, 2, KH>(p, x, w, y, s);
+    default: return launch_nb<T, 3, KH>(p, x, w, y, s);
   }
 }
 
@@ -399,8 +422,9 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
 }  // namespace
 
 bool slab_accepts(const ConvParams& p, int dtype) {
-  return (dtype == kF16 || dtype == kBF16) && p.groups == 1 && p.remap == 0 && p.sh == 1 &&
-         p.sw == 1 && p.eh == 1 && p.ew == 1 && p.cin % 32 == 0 && p.cout % 4 == 0 &&
+  return (dtype == kF16 || dtype == kBF16) && p.remap == 0 && p.sh == 1 && p.sw == 1 &&
+         p.eh == 1 && p.ew == 1 && p.cin_g % 32 == 0 && p.cout % 4 == 0 &&
+         (p.groups == 1 || p.cout_g % 64 == 0) &&
          p.kw <= kMaxKW && p.kh >= 2 && p.kh <= kMaxKH && p.kd <= 16;
 }
 

@@ -101,11 +101,12 @@ typedef enum {
   CONVFWD_PATH_GROUPED = 8, /* any dtype, G > 1 with C_in/G in {1, 2, 4, 8, 16}, C_out/G <= 16 and
                               C_out * K_d*K_h*K_w * C_in/G <= 16384 (depthwise and small groups):
                               one thread per (output position, group), fp32 FMA, filter in LDS */
-  CONVFWD_PATH_SLAB = 9    /* fp16/bf16, G = 1, C_in % 32 == 0, C_out % 4 == 0, stride and dilation 1
-                              along h and w, K_h in {2, 3}, K_w <= 3, K_d <= 16: tiles of 16
-                              output rows x 32 outputs (ragged at the ends); per (channel chunk, kd) the
-                              18 input rows those windows cover are staged in LDS once and all
-                              K_h * K_w taps read from them, MFMA */
+  CONVFWD_PATH_SLAB = 9    /* fp16/bf16, C_in/G % 32 == 0, C_out % 4 == 0, G = 1 or C_out/G % 64 == 0,
+                              stride and dilation 1 along h and w, K_h in {2, 3}, K_w <= 3,
+                              K_d <= 16: tiles of 16 output rows x 32 outputs (ragged at the
+                              ends) x 128 or 64 channels (64 within one group); per (channel
+                              chunk, kd) the 18 input rows those windows cover are staged in LDS
+                              once and all K_h * K_w taps read from them, MFMA */
 } convfwd_path;
 
 /* Problem descriptor.  All extents in elements. */

@@ -227,8 +227,8 @@ def test_grouped_problem_path_acceptance(path, ok):
     assert igc.lib().conv_fwd_path_ex(ctypes.byref(d), path, None, None, None, None) == (0 if ok else -3)
 
 
-# The slab path: fp16/bf16, G = 1, C_in % 32 == 0, C_out % 4 == 0, unit stride and no
-# dilation along h and w, W_out % 32 == 0, K_h in {2, 3}, K_w <= 3 (n = 0: only the rules run).
+# The slab path: fp16/bf16, C_in/G % 32 == 0, C_out % 4 == 0 and (G = 1 or C_out/G % 64 == 0),
+# unit stride and no dilation along h and w, K_h in {2, 3}, K_w <= 3 (n = 0: only the rules run).
 _SLAB_OK = dict(n=0, c_in=64, c_out=68, h=9, w=32)
 @pytest.mark.parametrize("change,ok", [
     ({}, True), ({"k_h": 2, "p_h": 0, "q_h": 0}, True), ({"k_w": 1, "p_w": 0, "q_w": 0}, True),
@@ -236,7 +236,8 @@ _SLAB_OK = dict(n=0, c_in=64, c_out=68, h=9, w=32)
     ({"k_h": 1, "p_h": 0, "q_h": 0}, False), ({"k_h": 4, "p_h": 2}, False), ({"k_w": 4, "p_w": 2}, False),
     ({"s_h": 2}, False), ({"e_h": 2, "p_h": 2, "q_h": 2}, False), ({"s_w": 2, "w": 63}, False),
     ({"w": 33}, True), ({"w": 7}, True), ({"c_in": 48}, False), ({"c_out": 66}, False), ({"dtype": 0}, False),
-    ({"groups": 2, "c_out": 64}, False),
+    ({"groups": 2, "c_out": 64}, False),                     # 32 outputs per group
+    ({"groups": 2, "c_out": 128}, True),                     # 64 outputs per group: 64-wide tiles
 ])
 def test_slab_path_acceptance(change, ok):
     d = _desc_ex(**{**_SLAB_OK, **change})

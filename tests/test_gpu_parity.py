@@ -306,6 +306,10 @@ VARIANTS = [
      ((4, 4), (2, 2)), (2, 1), 40),
     ("depthwise3d_fp32_k3_ragged", "fp32", (2, 6, 7, 37, 12), (12, 3, 3, 3, 1), (2, 1, 1),
      ((1, 1), (1, 1), (1, 1)), (1, 1, 1), 12),
+    ("grouped3d_fp16_g2_cg64_og64", "fp16", (1, 3, 18, 35, 128), (128, 3, 3, 3, 64), (1, 1, 1),
+     ((1, 1), (1, 1), (1, 1)), (1, 1, 1), 2),
+    ("grouped2d_bf16_g4_cg32_og64", "bf16", (2, 20, 40, 128), (256, 3, 3, 32), (1, 1),
+     ((1, 1), (1, 1)), (1, 1), 4),
     ("depthwise2d_fp16_k3_odd_h", "fp16", (2, 15, 21, 32), (32, 3, 3, 1), (1, 1),
      ((1, 1), (1, 1)), (1, 1), 32),
     ("depthwise2d_fp16_k7_c64", "fp16", (2, 20, 35, 64), (64, 7, 7, 1), (1, 1),
@@ -328,8 +332,8 @@ def _v_accepts(v, path):
         return (half and g == 1 and dil[-1] == 1 and xs[-1] % 32 == 0 and ws[0] % 4 == 0
                 and st[-1] == 1 and ow % 32 == 0 and ws[-2] <= 5)
     if path == "slab":
-        return (half and g == 1 and dil[-1] == 1 and dil[-2] == 1 and xs[-1] % 32 == 0
-                and ws[0] % 4 == 0 and st[-1] == 1 and st[-2] == 1
+        return (half and (g == 1 or cout_g % 64 == 0) and dil[-1] == 1 and dil[-2] == 1
+                and cin_g % 32 == 0 and ws[0] % 4 == 0 and st[-1] == 1 and st[-2] == 1
                 and ws[-2] <= 3 and ws[-3] in (2, 3))
     return True
 
