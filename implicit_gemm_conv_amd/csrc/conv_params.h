@@ -93,4 +93,7 @@ bool runs_accepts(const ConvParams& p, int dtype);
 bool grouped_accepts(const ConvParams& p, int dtype);
 bool slab_accepts(const ConvParams& p, int dtype);
 
+// Compute units of the current device (looked up once per device).
+int device_cus();
+
 }  // namespace convfwd

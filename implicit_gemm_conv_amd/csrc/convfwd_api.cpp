@@ -14,6 +14,27 @@
 
 #include "conv_params.h"
 
+namespace convfwd {
+
+// Compute units of the current device, looked up once per device (relaxed
+// atomics: threads that race on the first lookup store the same value).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    v = cus;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+}  // namespace convfwd
+
 using convfwd::ConvParams;
 
 namespace {

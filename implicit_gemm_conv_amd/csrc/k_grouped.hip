@@ -31,8 +31,6 @@
 // and a window row's loads gathered before its FMAs.
 #include "conv_device.h"
 
-#include <atomic>
-
 namespace convfwd {
 
 namespace {
@@ -301,23 +299,6 @@ __global__ __launch_bounds__(256) void conv_grouped_kernel(ConvParams p, const T
     for (int o = 0; o < kMaxOG; ++o)
       if (o < og) yp[o] = from_f32<T>(acc[o]);
   }
-}
-
-// Compute units of the current device, looked up once per device (relaxed
-// atomics: threads that race on the first lookup store the same value).
-int device_cus() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cached[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    v = cus;
-    cached[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
 }
 
 template <typename T, int CG, int KW, int SW, int TH>

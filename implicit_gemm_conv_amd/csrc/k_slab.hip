@@ -1,6 +1,7 @@
 // k_slab.hip -- implicit GEMM whose K steps read the w-taps and the h-taps of
 // a filter plane from one staged block of input rows (fp16/bf16, C_in % 32 ==
-// 0, unit stride and no dilation along h and w, K_h in {2, 3}, K_w <= 3).
+// 0, unit stride along h and w, K_h in {2, 3}, K_w <= 3; dilation 1 along h
+// and w, or 2 along both with a 3 x 3 plane).
 //
 // The classic implicit GEMM ("Convolutions" tutorial, section 5) gathers the
 // A tile of every tap afresh, although the tiles of neighbouring taps are the
@@ -22,6 +23,10 @@
 // must land by the barrier that starts the next plane; the filter slice of
 // step s + 1 goes out right after the barrier that starts step s.  A slab is
 // 40 wave loads of 16 positions (612 needed), the filter slices of a step 24 KB.
+// A dilated plane ("Convolution variants worth knowing": taps e positions apart)
+// changes only where the taps read: at e = 2 output row g takes slab row
+// g + 2 kh and position r + 2 kw, from a slab of 20 rows x 36 positions (48
+// wave loads, 48 KB a stage).
 //
 // Eight waves, two per SIMD: wave v owns output rows 4 (v % 4) .. + 3 of the
 // tile (128 GEMM rows) x channels 64 (v / 4) .. + 63 = 4 x 2 blocks of
@@ -52,15 +57,23 @@ constexpr int kRawBufferFlags = 0x00020000;
 constexpr int kSeg = 32;                            // outputs along w per tile row
 constexpr int kRowsOut = 16;                        // output rows along h per tile
 constexpr int kBM = kSeg * kRowsOut;                // 512 GEMM rows
-constexpr int kSW = 34;                             // slab positions per row (32 + K_w - 1 <= 34)
 constexpr int kMaxKW = 3;
 constexpr int kMaxKH = 3;
-constexpr int kRowsIn = kRowsOut + kMaxKH - 1;      // 18 slab rows
 constexpr int kRowB = 64;                           // bytes per position / filter row (32 channels)
-constexpr int kA_LOADS = 5;                         // 16-position wave loads per wave per slab
-constexpr int kSlabBytes = 8 * kA_LOADS * 16 * kRowB;   // 40 KB (18 x 34 positions and a spare tail)
 constexpr int kLdsBytes = 160 * 1024;
-static_assert(8 * kA_LOADS * 16 >= kRowsIn * kSW, "slab loads cover the slab");
+
+// Slab extents at dilation E along h and w: positions per row (E = 1: 34,
+// E = 2: 36), rows (18, 20), 16-position wave loads per wave (5, 6) and the
+// bytes of one slab stage (40, 48 KB; the loads may run past the slab into a
+// spare tail).
+template <int E>
+struct SlabGeom {
+  static constexpr int SW = kSeg + (kMaxKW - 1) * E;
+  static constexpr int ROWS = kRowsOut + (kMaxKH - 1) * E;
+  static constexpr int LOADS = (ROWS * SW + 127) / 128;
+  static constexpr int BYTES = 8 * LOADS * 16 * kRowB;
+  static_assert(8 * LOADS * 16 >= ROWS * SW, "slab loads cover the slab");
+};
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
@@ -81,7 +94,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // physical 16-byte chunk of logical chunk c at slab position o (or filter row o)
 __device__ __forceinline__ int swz(int o, int c) { return c ^ ((o >> 2) & 3); }
 
-template <typename T, int KW, int KH, int NB>
+template <typename T, int KW, int KH, int NB, int E>
 __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T* __restrict__ x,
                                                            const T* __restrict__ w,
                                                            T* __restrict__ y, int tiles_n,
@@ -89,6 +102,10 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef typename Vec8<T>::type V8;
   static_assert(NB == 128 || NB == 64, "channels per tile");
+  static_assert(E == 1 || (E == 2 && KW == 3 && KH == 3), "dilation along h and w");
+  constexpr int kSW = SlabGeom<E>::SW;
+  constexpr int kA_LOADS = SlabGeom<E>::LOADS;
+  constexpr int kSlabBytes = SlabGeom<E>::BYTES;
   constexpr int WR = NB == 128 ? 4 : 2;            // output rows (A fragments) per wave
   constexpr int NM = 2 * WR;                       // MFMAs per block per wave
   constexpr int B_ROWS = KW * NB;                  // filter rows per step
@@ -150,7 +167,7 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
     const int c = swz(o, lane & 3);                    // logical chunk this lane fetches
     const int ih = y0 + r, iw = x0 + o;
     uint32_t base = 0, mask = 0;
-    if (r < kRowsOut + KH - 1 && o < kSeg + KW - 1 && ih >= 0 && ih < p.h && iw >= 0 && iw < p.w) {
+    if (r < kRowsOut + (KH - 1) * E && o < kSeg + (KW - 1) * E && ih >= 0 && ih < p.h && iw >= 0 && iw < p.w) {
       mask = dmask;
       base = (uint32_t)(((img * p.xs_n + z0 * p.xs_d + ih * p.xs_h + iw * p.xs_w) + cbase + c * 8) * 2);
     }
@@ -225,7 +242,7 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
   for (int kw = 0; kw < KW; ++kw)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int o = r + kw;
+      const int o = r + kw * E;
       a_addr[kw][ks] = (wm * WR * kSW + o) * kRowB + swz(o, 2 * ks + g2) * 16;
     }
 #pragma unroll
@@ -325,8 +342,8 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
         constexpr int kh = decltype(khc)::value;
         const char* sb = smem + B_BASE + fs * B_BYTES;
         const char* nb = smem + B_BASE + (fs ^ 1) * B_BYTES;
-        const char* sak = sa + kh * kSW * kRowB;
-        const char* nak = kh + 1 < KH ? sa + (kh + 1) * kSW * kRowB : sn;
+        const char* sak = sa + kh * E * kSW * kRowB;
+        const char* nak = kh + 1 < KH ? sa + (kh + 1) * E * kSW * kRowB : sn;
         run_step(sak, sb, nak, nb, khc, std::integral_constant<bool, kFinal && kh + 1 == KH>{});
         fs ^= 1;
       };
@@ -386,23 +403,28 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <typename T, int KW, int KH, int NB>
+template <typename T, int KW, int KH, int NB, int E>
 hipError_t launch_k(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   const int tiles_m = p.n * p.od * ((p.oh + kRowsOut - 1) / kRowsOut) * ((p.ow + kSeg - 1) / kSeg);
   const int tiles_n = (p.cout + NB - 1) / NB;
   const uint32_t xb = (uint32_t)((int64_t)p.n * p.xs_n * 2);
   const uint32_t wb = (uint32_t)((int64_t)p.cout * p.K * 2);
-  hipLaunchKernelGGL((conv_slab_kernel<T, KW, KH, NB>), dim3(tiles_m * tiles_n), dim3(512), 0, s, p,
+  hipLaunchKernelGGL((conv_slab_kernel<T, KW, KH, NB, E>), dim3(tiles_m * tiles_n), dim3(512), 0, s, p,
                      (const T*)x, (const T*)w, (T*)y, tiles_n, xb, wb);
   return hipGetLastError();
 }
 
-// 64-channel tiles for grouped layers (a tile stays inside one group) and for
-// C_out <= 64 (a 128-channel tile would leave half its columns idle).
-template <typename T, int KW, int KH>
+// 64-channel tiles for grouped layers (a tile stays inside one group), for
+// C_out <= 64 (a 128-channel tile would leave half its columns idle) and when
+// 128-channel tiles would be fewer than the compute units (one workgroup fits
+// a CU: (8, 64^2, 256) makes 128 of them, and 64-channel tiles run it faster
+// on all 256 CUs).
+template <typename T, int KW, int KH, int E = 1>
 hipError_t launch_nb(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
-  if (p.groups > 1 || p.cout <= 64) return launch_k<T, KW, KH, 64>(p, x, w, y, s);
-  return launch_k<T, KW, KH, 128>(p, x, w, y, s);
+  const int64_t tiles_m = (int64_t)p.n * p.od * ((p.oh + kRowsOut - 1) / kRowsOut) * ((p.ow + kSeg - 1) / kSeg);
+  if (p.groups > 1 || p.cout <= 64 || tiles_m * ((p.cout + 127) / 128) < device_cus())
+    return launch_k<T, KW, KH, 64, E>(p, x, w, y, s);
+  return launch_k<T, KW, KH, 128, E>(p, x, w, y, s);
 }
 
 template <typename T, int KH>
@@ -416,6 +438,7 @@ hipError_t launch_kh(const ConvParams& p, const void* x, const void* w, void* y,
 
 template <typename T>
 hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
+  if (p.eh == 2) return launch_nb<T, 3, 3, 2>(p, x, w, y, s);   // dilated 3 x 3
   return p.kh == 2 ? launch_kh<T, 2>(p, x, w, y, s) : launch_kh<T, 3>(p, x, w, y, s);
 }
 
@@ -423,7 +446,7 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
 
 bool slab_accepts(const ConvParams& p, int dtype) {
   return (dtype == kF16 || dtype == kBF16) && p.remap == 0 && p.sh == 1 && p.sw == 1 &&
-         p.eh == 1 && p.ew == 1 && p.cin_g % 32 == 0 && p.cout % 4 == 0 &&
+         p.eh == p.ew && (p.eh == 1 || (p.eh == 2 && p.kh == 3 && p.kw == 3)) && p.cin_g % 32 == 0 && p.cout % 4 == 0 &&
          (p.groups == 1 || p.cout_g % 64 == 0) &&
          p.kw <= kMaxKW && p.kh >= 2 && p.kh <= kMaxKH && p.kd <= 16;
 }

@@ -102,10 +102,11 @@ typedef enum {
                               C_out * K_d*K_h*K_w * C_in/G <= 16384 (depthwise and small groups):
                               one thread per (output position, group), fp32 FMA, filter in LDS */
   CONVFWD_PATH_SLAB = 9    /* fp16/bf16, C_in/G % 32 == 0, C_out % 4 == 0, G = 1 or C_out/G % 64 == 0,
-                              stride and dilation 1 along h and w, K_h in {2, 3}, K_w <= 3,
-                              K_d <= 16: tiles of 16 output rows x 32 outputs (ragged at the
-                              ends) x 128 or 64 channels (64 within one group); per (channel
-                              chunk, kd) the 18 input rows those windows cover are staged in LDS
+                              stride 1 along h and w, K_h in {2, 3}, K_w <= 3, K_d <= 16,
+                              dilation 1 along h and w or 2 along both with K_h = K_w = 3:
+                              tiles of 16 output rows x 32 outputs (ragged at the ends) x 128
+                              or 64 channels (64 within one group); per (channel chunk, kd) the
+                              input rows those windows cover (18, dilated 20) are staged in LDS
                               once and all K_h * K_w taps read from them, MFMA */
 } convfwd_path;
 

@@ -228,7 +228,8 @@ def test_grouped_problem_path_acceptance(path, ok):
 
 
 # The slab path: fp16/bf16, C_in/G % 32 == 0, C_out % 4 == 0 and (G = 1 or C_out/G % 64 == 0),
-# unit stride and no dilation along h and w, K_h in {2, 3}, K_w <= 3 (n = 0: only the rules run).
+# unit stride along h and w, K_h in {2, 3}, K_w <= 3, dilation 1 along h and w or 2 along both
+# with a 3 x 3 plane (n = 0: only the rules run).
 _SLAB_OK = dict(n=0, c_in=64, c_out=68, h=9, w=32)
 @pytest.mark.parametrize("change,ok", [
     ({}, True), ({"k_h": 2, "p_h": 0, "q_h": 0}, True), ({"k_w": 1, "p_w": 0, "q_w": 0}, True),
@@ -238,6 +239,12 @@ _SLAB_OK = dict(n=0, c_in=64, c_out=68, h=9, w=32)
     ({"w": 33}, True), ({"w": 7}, True), ({"c_in": 48}, False), ({"c_out": 66}, False), ({"dtype": 0}, False),
     ({"groups": 2, "c_out": 64}, False),                     # 32 outputs per group
     ({"groups": 2, "c_out": 128}, True),                     # 64 outputs per group: 64-wide tiles
+    ({"e_h": 2, "e_w": 2, "p_h": 2, "q_h": 2, "p_w": 2, "q_w": 2}, True),                  # dilated 3 x 3
+    ({"e_h": 2, "e_w": 2, "p_h": 2, "q_h": 2, "p_w": 2, "q_w": 2, "groups": 2, "c_out": 128}, True),
+    ({"e_h": 2, "e_w": 2, "k_w": 2, "p_h": 2, "q_h": 2, "p_w": 1, "q_w": 1}, False),     # dilated 3 x 2
+    ({"e_h": 2, "e_w": 2, "k_h": 2, "p_h": 1, "q_h": 1, "p_w": 2, "q_w": 2}, False),     # dilated 2 x 3
+    ({"e_h": 3, "e_w": 3, "p_h": 3, "q_h": 3, "p_w": 3, "q_w": 3}, False),
+    ({"e_w": 2, "p_w": 2, "q_w": 2}, False),                 # dilated along w only
 ])
 def test_slab_path_acceptance(change, ok):
     d = _desc_ex(**{**_SLAB_OK, **change})
@@ -256,6 +263,7 @@ def test_auto_path_for_variants():
     assert igc.select_path((2, 8, 8, 8, 32), (32, 3, 3, 3, 1), 1, 1, torch.float16, groups=32) == "grouped"
     assert igc.select_path((2, 8, 8, 8, 96), (96, 3, 3, 3, 3), 1, 1, torch.float16, groups=32) == "runs"
     assert igc.select_path((2, 16, 16, 64), (64, 3, 3, 64), 1, 2, torch.float16, dilation=2) == "main"
+    assert igc.select_path((8, 64, 64, 256), (256, 3, 3, 256), 1, 2, torch.float16, dilation=2) == "slab"
     assert igc.select_path((2, 8, 8, 32, 64), (64, 3, 3, 3, 64), 1, 1, torch.float16, dilation=(2, 2, 1)) == "strip"
 
 
