@@ -105,9 +105,11 @@ typedef enum {
                               stride 1 along h and w, K_h in {2, 3}, K_w <= 3, K_d <= 16,
                               dilation 1 along h and w or 2 along both with K_h = K_w = 3:
                               tiles of 16 output rows x 32 outputs (ragged at the ends) x 128
-                              or 64 channels (64 within one group); per (channel chunk, kd) the
-                              input rows those windows cover (18, dilated 20) are staged in LDS
-                              once and all K_h * K_w taps read from them, MFMA */
+                              or 64 channels (64 within one group, for C_out <= 64, and when
+                              128-channel tiles would be fewer than the device's compute
+                              units); per (channel chunk, kd) the input rows those windows
+                              cover (18, dilated 20) are staged in LDS once and all K_h * K_w
+                              taps read from them, MFMA */
 } convfwd_path;
 
 /* Problem descriptor.  All extents in elements. */
