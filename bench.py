@@ -276,7 +276,7 @@ def main():
                     help="in --sweep, time every path per shape first and use the fastest (conv_tune)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the convolution would shard by batch or C_out with no exchange).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
