@@ -178,6 +178,24 @@ def select_path(x_shape, w_shape, stride=1, padding=0, dtype=torch.float16, dila
     return PATH_NAMES[_check(lib().conv_select_path_ex(ctypes.byref(d)))]
 
 
+def _check_filter(x_shape, w_shape, groups):
+    """w must have x's rank and C_in/groups input channels: the library sizes its reads of w
+    from the descriptor, so a filter of another shape would be read out of bounds or with the
+    wrong stride."""
+    if len(w_shape) != len(x_shape):
+        raise ValueError(f"x {tuple(x_shape)} and w {tuple(w_shape)} must have the same rank")
+    if groups < 1 or w_shape[-1] * groups != x_shape[-1]:
+        raise ValueError(f"w {tuple(w_shape)} must hold C_in/groups = {x_shape[-1]}/{groups} input "
+                         f"channels in its last dimension")
+
+
+def _check_out(out, shape, like, what="out"):
+    if tuple(out.shape) != tuple(shape) or out.dtype != like.dtype or not out.is_contiguous() \
+            or out.device != like.device:
+        raise ValueError(f"{what} must be a contiguous {like.dtype} tensor of shape {tuple(shape)} "
+                         f"on {like.device}")
+
+
 def conv_fwd(x: torch.Tensor, w: torch.Tensor, stride=1, padding=0, out: torch.Tensor = None,
              path: str = "auto", dilation=1, groups: int = 1) -> torch.Tensor:
     """Channels-last convolution forward on the GPU.
@@ -193,15 +211,15 @@ def conv_fwd(x: torch.Tensor, w: torch.Tensor, stride=1, padding=0, out: torch.T
         raise ValueError("conv_fwd runs on the GPU only: x and w must be device tensors")
     if x.device != w.device or x.dtype != w.dtype:
         raise ValueError("x and w must share device and dtype")
+    _check_filter(x.shape, w.shape, groups)
     x = x.contiguous()
     w = w.contiguous()
     d = make_desc_ex(tuple(x.shape), tuple(w.shape), stride, padding, dilation, groups, x.dtype)
     shape = out_shape(tuple(x.shape), tuple(w.shape), stride, padding, dilation, groups)
     if out is None:
         out = torch.empty(shape, dtype=x.dtype, device=x.device)
-    elif tuple(out.shape) != shape or out.dtype != x.dtype or not out.is_contiguous() \
-            or out.device != x.device:
-        raise ValueError(f"out must be a contiguous {x.dtype} tensor of shape {shape} on {x.device}")
+    else:
+        _check_out(out, shape, x)
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
         _check(lib().conv_fwd_path_ex(ctypes.byref(d), PATHS[path], x.data_ptr(), w.data_ptr(),
@@ -216,12 +234,15 @@ def tune(x: torch.Tensor, w: torch.Tensor, stride=1, padding=0, dilation=1, grou
     microseconds per launch).  Synchronises the current stream."""
     if not (x.is_cuda and w.is_cuda) or x.device != w.device or x.dtype != w.dtype:
         raise ValueError("tune needs x and w on one GPU with one dtype")
+    _check_filter(x.shape, w.shape, groups)
     x = x.contiguous()
     w = w.contiguous()
     d = make_desc_ex(tuple(x.shape), tuple(w.shape), stride, padding, dilation, groups, x.dtype)
     shape = out_shape(tuple(x.shape), tuple(w.shape), stride, padding, dilation, groups)
     if out is None:
         out = torch.empty(shape, dtype=x.dtype, device=x.device)
+    else:
+        _check_out(out, shape, x)
     us = ctypes.c_float(0.0)
     with torch.cuda.device(x.device):
         stream = torch.cuda.current_stream(x.device).cuda_stream
@@ -249,12 +270,13 @@ def bwd_data_filter(w: torch.Tensor, x_shape, stride=1, padding=0, dilation=1, g
     depends only on w and the problem, so it can be prepared once per filter."""
     if not w.is_cuda:
         raise ValueError("bwd_data_filter runs on the GPU only: w must be a device tensor")
+    _check_filter(tuple(x_shape), w.shape, groups)
     w = w.contiguous()
     d = make_desc_ex(tuple(x_shape), tuple(w.shape), stride, padding, dilation, groups, w.dtype)
     if out is None:
         out = torch.empty_like(w)
-    elif out.shape != w.shape or out.dtype != w.dtype or not out.is_contiguous() or out.device != w.device:
-        raise ValueError("out must be a contiguous tensor like w")
+    else:
+        _check_out(out, w.shape, w)
     with torch.cuda.device(w.device):
         stream = torch.cuda.current_stream(w.device).cuda_stream
         _check(lib().conv_bwd_data_filter_ex(ctypes.byref(d), w.data_ptr(), out.data_ptr(), stream))
@@ -275,18 +297,20 @@ def conv_bwd_data(dy: torch.Tensor, w: torch.Tensor, x_shape, stride=1, padding=
     if dy.device != w.device or dy.dtype != w.dtype:
         raise ValueError("dy and w must share device and dtype")
     x_shape = tuple(int(e) for e in x_shape)
+    _check_filter(x_shape, w.shape, groups)
     dy = dy.contiguous()
     y_shape = out_shape(x_shape, tuple(w.shape), stride, padding, dilation, groups)
     if tuple(dy.shape) != y_shape:
         raise ValueError(f"dy must have the forward output shape {y_shape}, got {tuple(dy.shape)}")
     if wt is None:
         wt = bwd_data_filter(w, x_shape, stride, padding, dilation, groups)
+    else:
+        _check_out(wt, w.shape, w, "wt (the rearranged filter)")
     d = make_desc_ex(x_shape, tuple(w.shape), stride, padding, dilation, groups, dy.dtype)
     if out is None:
         out = torch.empty(x_shape, dtype=dy.dtype, device=dy.device)
-    elif tuple(out.shape) != x_shape or out.dtype != dy.dtype or not out.is_contiguous() \
-            or out.device != dy.device:
-        raise ValueError(f"out must be a contiguous {dy.dtype} tensor of shape {x_shape} on {dy.device}")
+    else:
+        _check_out(out, x_shape, dy)
     with torch.cuda.device(dy.device):
         stream = torch.cuda.current_stream(dy.device).cuda_stream
         _check(lib().conv_bwd_data_path_ex(ctypes.byref(d), PATHS[path], dy.data_ptr(), wt.data_ptr(),

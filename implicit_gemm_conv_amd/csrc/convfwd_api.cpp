@@ -136,11 +136,36 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn) {
   return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
 }
 
+// Paths whose kernels move x, w and y in 16-byte pieces at offsets counted
+// from the base pointers (direct-to-LDS buffer loads, 16-byte stores): they
+// need all three tensors 16-byte aligned.  The runs, direct and grouped paths
+// need element alignment only (the grouped path checks for its 16-byte
+// kernel itself).
+bool needs_16(int path) {
+  switch (path) {
+    case CONVFWD_PATH_SLAB:
+    case CONVFWD_PATH_STRIP:
+    case CONVFWD_PATH_MAIN:
+    case CONVFWD_PATH_BRICK:
+    case CONVFWD_PATH_ROWS:
+    case CONVFWD_PATH_FLATK: return true;
+    default: return false;
+  }
+}
+
+bool aligned_to(const void* a, const void* b, const void* c, uintptr_t bytes) {
+  return (((uintptr_t)a | (uintptr_t)b | (uintptr_t)c) & (bytes - 1)) == 0;
+}
+
 // The brick path is available on request; on the measured shapes the
-// per-tap-gather main path is faster, so AUTO does not pick it.
-int auto_path(const ConvParams& p, int dtype) {
+// per-tap-gather main path is faster, so AUTO does not pick it.  With tensors
+// that are not all 16-byte aligned AUTO keeps to the paths that need element
+// alignment only (the unaligned-channel tail path, else direct), the
+// fall-back-rather-than-fail rule of the MLX pull request's dispatch.
+int auto_path(const ConvParams& p, int dtype, bool al16 = true) {
   // Few channels per group (down to depthwise): the memory-bound vector-ALU form.
   if (convfwd::grouped_accepts(p, dtype)) return CONVFWD_PATH_GROUPED;
+  if (!al16) return convfwd::runs_accepts(p, dtype) ? CONVFWD_PATH_RUNS : CONVFWD_PATH_DIRECT;
   // Once the w-taps share a strip (K_w >= 2): the slab path where the h-taps
   // share its staged rows too, else the strip path.  With K_w = 1 the strip
   // path is the main path with a larger tile and the main path is faster.
@@ -277,13 +302,17 @@ int run(const convfwd_desc_ex* desc, int path, const void* x, const void* w, voi
   int64_t xb, wb, yb;
   const int rc = make_params(desc, &p, &xb, &wb, &yb);
   if (rc != CONVFWD_OK) return rc;
+  const bool al16 = aligned_to(x, w, y, 16);
   Choice tuned;
-  const bool use_tuned = path == CONVFWD_PATH_AUTO && tuned_choice(*desc, p, &tuned);
-  if (path == CONVFWD_PATH_AUTO) path = use_tuned ? tuned.path : auto_path(p, desc->dtype);
+  bool use_tuned = path == CONVFWD_PATH_AUTO && tuned_choice(*desc, p, &tuned);
+  if (use_tuned && !al16 && needs_16(tuned.path)) use_tuned = false;
+  if (path == CONVFWD_PATH_AUTO) path = use_tuned ? tuned.path : auto_path(p, desc->dtype, al16);
   if (!path_accepts(path, p, desc->dtype)) return CONVFWD_ERR_UNSUPPORTED;
+  if (!al16 && needs_16(path)) return CONVFWD_ERR_UNSUPPORTED;   // a forced 16-byte path
   if (p.n == 0) return CONVFWD_OK;  // empty batch: nothing to read or write
   if (!x || !w || !y) return CONVFWD_ERR_NULL;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb)) return CONVFWD_ERR_ALIAS;
+  if (!aligned_to(x, w, y, (uintptr_t)elem_bytes(desc->dtype))) return CONVFWD_ERR_MISALIGNED;
   const hipError_t e = use_tuned ? launch_choice(tuned, p, desc->dtype, x, w, y, (hipStream_t)stream)
                                  : launch_path(path, p, desc->dtype, x, w, y, (hipStream_t)stream);
   if (e != hipSuccess) return CONVFWD_ERR_LAUNCH;
@@ -300,17 +329,20 @@ int run_tune(const convfwd_desc_ex* desc, const void* x, const void* w, void* y,
   if (p.n == 0) return auto_path(p, desc->dtype);   // nothing to time
   if (!x || !w || !y) return CONVFWD_ERR_NULL;
   if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb)) return CONVFWD_ERR_ALIAS;
-  // candidates: every accepting path, the main path once per tile configuration;
-  // the direct path only when nothing else takes the problem or it is small
+  if (!aligned_to(x, w, y, (uintptr_t)elem_bytes(desc->dtype))) return CONVFWD_ERR_MISALIGNED;
+  // candidates: every accepting path (the 16-byte ones only for 16-byte aligned
+  // tensors), the main path once per tile configuration; the direct path only
+  // when nothing else takes the problem or it is small
+  const bool al16 = aligned_to(x, w, y, 16);
   Choice cand[64];
   int nc = 0;
   const int paths[] = {CONVFWD_PATH_SLAB, CONVFWD_PATH_STRIP, CONVFWD_PATH_GROUPED, CONVFWD_PATH_ROWS,
                        CONVFWD_PATH_RUNS, CONVFWD_PATH_FLATK, CONVFWD_PATH_BRICK};
   for (int q : paths)
-    if (path_accepts(q, p, desc->dtype)) cand[nc++] = Choice{q, 0, 0.f};
+    if (path_accepts(q, p, desc->dtype) && (al16 || !needs_16(q))) cand[nc++] = Choice{q, 0, 0.f};
   int ncfg = 0;
   const int* cfgs = convfwd::main_tile_configs(&ncfg);
-  for (int i = 0; i < ncfg; ++i)
+  for (int i = 0; i < ncfg && al16; ++i)
     if (convfwd::main_config_accepts(p, desc->dtype, cfgs[i])) cand[nc++] = Choice{CONVFWD_PATH_MAIN, cfgs[i], 0.f};
   const double macs = (double)p.M * p.cout_g * p.K;
   if (nc == 0 || macs < 1e8) cand[nc++] = Choice{CONVFWD_PATH_DIRECT, 0, 0.f};
@@ -469,12 +501,13 @@ int64_t phase_filter_offset(const BwdPlan& b, int rd, int rh, int rw) {
 // Path for one phase: AUTO takes the forward choice when the phase writes a
 // dense dx with non-negative pads (unit stride), else main, runs or direct,
 // the kernels that write remapped rows.  A phase without taps writes zeros
-// through the direct kernel.
-int phase_path(const ConvParams& q, int path, int dtype) {
+// through the direct kernel.  al16: dy, the phase's filter block and dx are
+// all 16-byte aligned (else only the element-aligned paths run).
+int phase_path(const ConvParams& q, int path, int dtype, bool al16) {
   if (q.ntaps == 0) return CONVFWD_PATH_DIRECT;
-  if (path != CONVFWD_PATH_AUTO) return path_accepts(path, q, dtype) ? path : -1;
-  if (!q.remap && q.pd >= 0 && q.ph >= 0 && q.pw >= 0) return auto_path(q, dtype);
-  if (convfwd::main_accepts(q, dtype)) return CONVFWD_PATH_MAIN;
+  if (path != CONVFWD_PATH_AUTO) return path_accepts(path, q, dtype) && (al16 || !needs_16(path)) ? path : -1;
+  if (!q.remap && q.pd >= 0 && q.ph >= 0 && q.pw >= 0) return auto_path(q, dtype, al16);
+  if (al16 && convfwd::main_accepts(q, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::runs_accepts(q, dtype)) return CONVFWD_PATH_RUNS;
   return CONVFWD_PATH_DIRECT;
 }
@@ -488,19 +521,24 @@ int run_bwd_data(const convfwd_desc_ex* desc, int path, const void* dy, const vo
   const int rc = make_bwd_plan(desc, &b);
   if (rc != CONVFWD_OK) return rc;
   const ConvParams& f = b.fwd;
+  const int eb = elem_bytes(desc->dtype);
+  // whether phase (rd, rh, rw)'s tensors (dy, its filter block, dx) are 16-byte aligned
+  auto phase_al16 = [&](int rd, int rh, int rw) {
+    return aligned_to(dy, (const char*)wt + phase_filter_offset(b, rd, rh, rw) * eb, dx, 16);
+  };
   // every phase must be runnable before the first launch
   for (int rd = 0; rd < f.sd; ++rd)
     for (int rh = 0; rh < f.sh; ++rh)
       for (int rw = 0; rw < f.sw; ++rw) {
         const ConvParams q = phase_params(b, rd, rh, rw);
         if (q.od == 0 || q.oh == 0 || q.ow == 0) continue;
-        if (phase_path(q, path, desc->dtype) < 0) return CONVFWD_ERR_UNSUPPORTED;
+        if (phase_path(q, path, desc->dtype, phase_al16(rd, rh, rw)) < 0) return CONVFWD_ERR_UNSUPPORTED;
       }
   if (f.n == 0) return CONVFWD_OK;
   if (!dy || !wt || !dx) return CONVFWD_ERR_NULL;
   if (overlaps(dx, b.x_bytes, dy, b.y_bytes) || overlaps(dx, b.x_bytes, wt, b.w_bytes))
     return CONVFWD_ERR_ALIAS;
-  const int eb = elem_bytes(desc->dtype);
+  if (!aligned_to(dy, wt, dx, (uintptr_t)eb)) return CONVFWD_ERR_MISALIGNED;
   hipStream_t s = (hipStream_t)stream;
   // Phases on the main path share one launch (their start-up and tails
   // overlap); the others run one launch each.
@@ -513,7 +551,7 @@ int run_bwd_data(const convfwd_desc_ex* desc, int path, const void* dy, const vo
         const ConvParams q = phase_params(b, rd, rh, rw);
         if (q.od == 0 || q.oh == 0 || q.ow == 0) continue;
         const int64_t off = phase_filter_offset(b, rd, rh, rw) * eb;
-        const int qp = phase_path(q, path, desc->dtype);
+        const int qp = phase_path(q, path, desc->dtype, phase_al16(rd, rh, rw));
         if (qp == CONVFWD_PATH_MAIN && q.remap && nbatch < (int)(sizeof(batch) / sizeof(batch[0]))) {
           batch[nbatch] = q;
           batch_off[nbatch++] = (uint32_t)off;
@@ -544,6 +582,7 @@ int run_bwd_filter(const convfwd_desc_ex* desc, const void* w, void* wt, void* s
   if (rc != CONVFWD_OK) return rc;
   if (!w || !wt) return CONVFWD_ERR_NULL;
   if (overlaps(wt, b.w_bytes, w, b.w_bytes)) return CONVFWD_ERR_ALIAS;
+  if (!aligned_to(w, wt, wt, (uintptr_t)elem_bytes(desc->dtype))) return CONVFWD_ERR_MISALIGNED;
   if (convfwd::launch_bwd_filter(b.geom, desc->dtype, w, wt, (hipStream_t)stream) != hipSuccess)
     return CONVFWD_ERR_LAUNCH;
   return CONVFWD_OK;
@@ -671,6 +710,7 @@ const char* conv_strerror(int code) {
     case CONVFWD_ERR_TOO_LARGE: return "too large: a tensor reaches 2^31 bytes or M reaches 2^31";
     case CONVFWD_ERR_ALIAS: return "the output overlaps an input";
     case CONVFWD_ERR_LAUNCH: return "kernel launch failed";
+    case CONVFWD_ERR_MISALIGNED: return "a tensor pointer is not aligned to its element size";
     default: return "unknown error code";
   }
 }

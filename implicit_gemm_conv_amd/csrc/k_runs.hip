@@ -275,8 +275,11 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // loads past the end
 
-  // Epilogue: lane holds D[n = 4*fg + i][m = fr] of each 16x16 block.
-  const bool vec_ok = (p.cout & 3) == 0 && (p.cout_g & 3) == 0;
+  // Epilogue: lane holds D[n = 4*fg + i][m = fr] of each 16x16 block.  Runs
+  // of 4 channels go out as one store when they are aligned to its size (y
+  // itself may be only element-aligned on this path).
+  const bool vec_ok =
+      (p.cout & 3) == 0 && (p.cout_g & 3) == 0 && (((uintptr_t)y & (uintptr_t)(4 * EB - 1)) == 0);
 #pragma unroll
   for (int a = 0; a < FM; ++a) {
     const int m = m0 + wave * TM + a * 16 + fr;

@@ -73,7 +73,8 @@ enum {
   CONVFWD_ERR_UNSUPPORTED = -3, /* unknown dtype, or a path that cannot take this problem */
   CONVFWD_ERR_TOO_LARGE = -4,   /* a tensor of 2^31 bytes or more, or M >= 2^31 */
   CONVFWD_ERR_ALIAS = -5,       /* y's byte range overlaps x or w */
-  CONVFWD_ERR_LAUNCH = -6       /* the HIP runtime refused the launch */
+  CONVFWD_ERR_LAUNCH = -6,      /* the HIP runtime refused the launch */
+  CONVFWD_ERR_MISALIGNED = -7   /* a tensor pointer not aligned to its element size */
 };
 
 /* Kernel paths.  AUTO lets the library choose; the others force one (for
@@ -142,15 +143,24 @@ typedef struct {
  * touches the GPU.  Returns CONVFWD_OK or a validation error. */
 int conv_out_shape(const convfwd_desc* desc, int64_t out[5]);
 
-/* The path CONVFWD_PATH_AUTO would take for this descriptor (a positive
- * convfwd_path), or a negative validation error.  Host only. */
+/* The path CONVFWD_PATH_AUTO would take for this descriptor with 16-byte
+ * aligned tensors (a positive convfwd_path), or a negative validation error.
+ * Host only. */
 int conv_select_path(const convfwd_desc* desc);
 
 /* y = conv(x, w) on `stream` (a hipStream_t; NULL means the null stream of the
  * current device).  x, w, y are device pointers on the current device, laid
- * out as above, with at least 2-byte (fp16/bf16) or 4-byte (fp32) alignment.
- * Asynchronous: returns after the launch.  With N = 0 it launches nothing and
- * returns CONVFWD_OK without reading the pointers. */
+ * out as above, each aligned to its element size (2 bytes for fp16/bf16, 4 for
+ * fp32; else CONVFWD_ERR_MISALIGNED).  The fast paths (slab, strip, main,
+ * brick, rows, flatk) move 16-byte pieces counted from the base pointers and
+ * need x, w and y all 16-byte aligned: with a tensor that is not, AUTO takes
+ * the unaligned-channel tail path (runs) or, if that cannot take the
+ * problem, direct, and a forced 16-byte path returns CONVFWD_ERR_UNSUPPORTED
+ * (the MLX pull request's dispatch falls back rather than failing).  Tensors
+ * from an allocator are 256-byte aligned; a view at an element offset may not
+ * be.  Asynchronous: returns after the launch.  With N = 0 it launches nothing
+ * and returns CONVFWD_OK without reading the pointers (a forced path must
+ * still accept the problem). */
 int conv_fwd(const convfwd_desc* desc, const void* x, const void* w, void* y, void* stream);
 
 /* As conv_fwd, but on the given path; CONVFWD_ERR_UNSUPPORTED if that path

@@ -324,3 +324,72 @@ def test_tune_table_host_rules():
         lib.conv_select_path_ex(ctypes.byref(empty))
     assert lib.conv_tuned_path_ex(ctypes.byref(empty)) == 0
     assert igc.tuned_path((2, 4, 5, 6, 8), (4, 3, 3, 3, 8), 1, 1) is None
+
+
+# ---- pointer alignment (host-side checks only: every call below returns before a launch) ----
+
+def test_forced_16_byte_paths_refuse_tensors_not_16_byte_aligned():
+    """The slab, strip and main kernels move 16-byte pieces counted from the base pointers:
+    forced onto them, an element-aligned but not 16-byte-aligned x, w or y is refused with
+    UNSUPPORTED before any launch (AUTO would take the tail path instead)."""
+    lib = igc.lib()
+    d = _desc(n=1, d=4, h=6, w=32, c_in=64, c_out=64)     # slab, strip and main all take it
+    base = 1 << 24
+    x, w, y = base, base + (1 << 22), base + (1 << 23)
+    for path in (1, 6, 9):
+        for dx, dw, dy in ((2, 0, 0), (0, 2, 0), (0, 0, 2), (8, 8, 8)):
+            assert lib.conv_fwd_path(ctypes.byref(d), path, x + dx, w + dw, y + dy, None) == -3, (path, dx, dw, dy)
+    # the same pointers aligned pass every host check (a forced path with n = 0 launches nothing)
+    d0 = _desc(n=0, d=4, h=6, w=32, c_in=64, c_out=64)
+    for path in (1, 6, 9):
+        assert lib.conv_fwd_path(ctypes.byref(d0), path, x, w, y, None) == 0
+    # the descriptor-only choice assumes aligned tensors
+    assert lib.conv_select_path(ctypes.byref(d)) == 6   # strip: 6 of 16 slab rows would be used
+
+
+def test_pointers_not_aligned_to_their_element_are_rejected():
+    lib = igc.lib()
+    base = 1 << 24
+    x, w, y = base, base + (1 << 22), base + (1 << 23)
+    d16 = _desc(n=1, d=4, h=6, w=32, c_in=64, c_out=64)
+    assert lib.conv_fwd(ctypes.byref(d16), x + 1, w, y, None) == -7
+    assert lib.conv_fwd_path(ctypes.byref(d16), 7, x, w + 1, y, None) == -7   # runs
+    assert lib.conv_fwd_path(ctypes.byref(d16), 4, x, w, y + 3, None) == -7   # direct
+    d32 = _desc(n=1, d=4, h=6, w=8, c_in=16, c_out=32, dtype=0)
+    assert lib.conv_fwd(ctypes.byref(d32), x + 2, w, y, None) == -7
+    assert lib.conv_tune(ctypes.byref(d16), x, w, y + 1, None, 5, None) == -7
+    assert lib.conv_strerror(-7).decode().startswith("a tensor pointer")
+
+
+def test_bwd_data_alignment_rules():
+    lib = igc.lib()
+    base = 1 << 24
+    dy, wt, dx = base, base + (1 << 22), base + (1 << 23)
+    ex = _desc_ex(n=1, c_in=8, c_out=64, s_d=2, s_h=2, s_w=2)
+    # forced main needs every phase's tensors 16-byte aligned
+    assert lib.conv_bwd_data_path_ex(ctypes.byref(ex), 1, dy + 2, wt, dx, None) == -3
+    assert lib.conv_bwd_data_path_ex(ctypes.byref(ex), 1, dy, wt, dx + 8, None) == -3
+    # not even element-aligned: rejected on every path, before any launch
+    assert lib.conv_bwd_data_ex(ctypes.byref(ex), dy + 1, wt, dx, None) == -7
+    assert lib.conv_bwd_data_path_ex(ctypes.byref(ex), 4, dy, wt + 1, dx, None) == -7
+    assert lib.conv_bwd_data_filter_ex(ctypes.byref(ex), dy + 1, wt, None) == -7
+
+
+def test_binding_checks_filter_and_buffers_before_any_launch():
+    """The binding compares w with x (rank, C_in/groups channels) and a caller's out / wt
+    buffers with the shape, dtype and device the call will write or read: the library sizes
+    every access from the descriptor, so a mismatch must be caught before the call."""
+    igc._check_filter((1, 4, 4, 4, 64), (8, 3, 3, 3, 64), 1)
+    igc._check_filter((1, 4, 4, 4, 64), (8, 3, 3, 3, 32), 2)
+    with pytest.raises(ValueError):
+        igc._check_filter((1, 4, 4, 4, 64), (8, 3, 3, 3, 32), 1)       # half the channels
+    with pytest.raises(ValueError):
+        igc._check_filter((1, 4, 4, 4, 64), (8, 3, 3, 3, 128), 1)      # twice the channels
+    with pytest.raises(ValueError):
+        igc._check_filter((1, 4, 4, 64), (8, 3, 3, 3, 64), 1)          # rank
+    like = torch.zeros(2, 3, dtype=torch.float16)
+    igc._check_out(torch.zeros(4, 5, dtype=torch.float16), (4, 5), like)
+    for bad in (torch.zeros(4, 6, dtype=torch.float16), torch.zeros(4, 5, dtype=torch.bfloat16),
+                torch.zeros(5, 4, dtype=torch.float16).t()):
+        with pytest.raises(ValueError):
+            igc._check_out(bad, (4, 5), like)
