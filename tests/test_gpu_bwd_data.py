@@ -134,19 +134,16 @@ def test_bwd_data_writes_every_position_and_nothing_else():
 
 
 @pytest.mark.parametrize("name", sorted(BWD_WORKLOADS))
-def test_bwd_data_workloads_full_size_sampled(name):
-    """The backward-data workloads at full size, as bench.py --sweep runs them, checked on
-    sampled input positions the oracle computes one by one."""
+def test_bwd_data_workloads_full_size(name):
+    """The backward-data workloads at full size, as bench.py --sweep runs them, every input
+    position compared with the oracle."""
     wl = BWD_WORKLOADS[name]
     print(f"[bwd full] {name}", flush=True)
     x, w = make_inputs(wl, DEV)          # x here is dy: the shapes come from the workload
     dx = igc.conv_bwd_data(x, w, wl.dx_shape, wl.stride, wl.padding)
     torch.cuda.synchronize()
-    flat = dx.reshape(-1, dx.shape[-1])
-    rng = np.random.default_rng(wl.seed_x)
-    rows = np.unique(np.concatenate([rng.integers(0, flat.shape[0], 2048), [0, flat.shape[0] - 1]]))
     ref = oracle.conv_bwd_data(oracle.to_float64(x), oracle.to_float64(w), wl.dx_shape, wl.stride,
-                               wl.padding, rows=rows)
-    got = oracle.to_float64(flat[torch.from_numpy(rows).to(DEV)])
-    assert_parity(got, ref, wl.dtype, name)
-    assert torch.isfinite(dx.float()).all()
+                               wl.padding)
+    e = assert_parity(oracle.to_float64(dx), ref, wl.dtype, name)
+    print(f"[bwd full] {name} outputs={ref.size} l2_rel={e['l2_rel']:.2e} max_rel={e['max_rel']:.2e}",
+          flush=True)
