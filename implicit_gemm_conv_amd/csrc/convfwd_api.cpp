@@ -523,8 +523,10 @@ int run_bwd_data(const convfwd_desc_ex* desc, int path, const void* dy, const vo
   const ConvParams& f = b.fwd;
   const int eb = elem_bytes(desc->dtype);
   // whether phase (rd, rh, rw)'s tensors (dy, its filter block, dx) are 16-byte aligned
+  // (integer arithmetic: wt may be NULL for an empty batch)
   auto phase_al16 = [&](int rd, int rh, int rw) {
-    return aligned_to(dy, (const char*)wt + phase_filter_offset(b, rd, rh, rw) * eb, dx, 16);
+    const uintptr_t wq = (uintptr_t)wt + (uintptr_t)(phase_filter_offset(b, rd, rh, rw) * eb);
+    return aligned_to(dy, (const void*)wq, dx, 16);
   };
   // every phase must be runnable before the first launch
   for (int rd = 0; rd < f.sd; ++rd)

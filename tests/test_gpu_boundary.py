@@ -206,3 +206,22 @@ def test_plain_conv_fwd_entry_point(case):
     assert rc == 0, igc.lib().conv_strerror(rc)
     torch.cuda.synchronize()
     assert_parity(oracle.to_float64(y), _ref(x, w, st, pd, groups=g), dtype, name)
+
+
+@pytest.mark.parametrize("case", CANARY, ids=[f"{c[0]}_{c[1]}_{i}" for i, c in enumerate(CANARY)])
+def test_repeated_launches_are_bit_identical(case):
+    """Three launches of the same path on the same inputs, each preceded by a different
+    unrelated launch (so the machine state and the order of work around them differ), give
+    bit-identical results: a race on a staged LDS buffer would show as a difference."""
+    path, dtype, xs, ws, st, pd, g = case
+    x, w = _inputs(f"repeat{xs}{ws}", dtype, xs, ws)
+    other_x, other_w = _inputs("repeat_other", "fp16", (2, 6, 7, 9, 64), (64, 3, 3, 3, 64))
+    outs = []
+    for i in range(3):
+        for _ in range(i):
+            igc.conv_fwd(other_x, other_w, 1, 1, path=("main", "slab", "runs")[i])
+        outs.append(igc.conv_fwd(x, w, st, pd, path=path, groups=g))
+    torch.cuda.synchronize()
+    view = torch.int32 if dtype == "fp32" else torch.int16
+    for o in outs[1:]:
+        assert torch.equal(o.view(view), outs[0].view(view))
