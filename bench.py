@@ -51,6 +51,9 @@ _COMMON = ["implicit_gemm_conv_amd/csrc/conv_device.h", "implicit_gemm_conv_amd/
 KERNELS = {
     "slab": ("conv_slab_kernel<fp16, K_w=3, K_h=3>: 16x32-output x 128-channel tile, 32x32x16 MFMA",
              ["implicit_gemm_conv_amd/csrc/k_slab.hip", *_COMMON]),
+    "phase": ("conv_phase_kernel<fp16, K_h=3, K_w=3>: 8x16-output x 64-channel tile, stride-phase "
+              "staging, 32x32x16 MFMA",
+              ["implicit_gemm_conv_amd/csrc/k_phase.hip", *_COMMON]),
     "strip": ("conv_strip_kernel<fp16, K_w=3>: 512x128 tile, 32x32x16 MFMA",
               ["implicit_gemm_conv_amd/csrc/k_strip.hip", *_COMMON]),
     "main": ("conv_main_kernel<fp16>: 128x128 tile, BK=64, 16x16x32 MFMA",

@@ -58,6 +58,8 @@ hipError_t launch_grouped(const ConvParams& p, int dtype, const void* x, const v
                           hipStream_t s);
 hipError_t launch_slab(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
                        hipStream_t s);
+hipError_t launch_phase(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                        hipStream_t s);
 
 // Backward-data filter rearrangement (see k_bwd.hip): per dimension the stride
 // s, dilation e, low pad p, filter extent K and, per stride phase r < s, the
@@ -92,6 +94,7 @@ bool strip_accepts(const ConvParams& p, int dtype);
 bool runs_accepts(const ConvParams& p, int dtype);
 bool grouped_accepts(const ConvParams& p, int dtype);
 bool slab_accepts(const ConvParams& p, int dtype);
+bool phase_accepts(const ConvParams& p, int dtype);
 
 // Compute units of the current device (looked up once per device).
 int device_cus();

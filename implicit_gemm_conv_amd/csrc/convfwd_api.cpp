@@ -148,7 +148,8 @@ bool needs_16(int path) {
     case CONVFWD_PATH_MAIN:
     case CONVFWD_PATH_BRICK:
     case CONVFWD_PATH_ROWS:
-    case CONVFWD_PATH_FLATK: return true;
+    case CONVFWD_PATH_FLATK:
+    case CONVFWD_PATH_PHASE: return true;
     default: return false;
   }
 }
@@ -176,6 +177,8 @@ int auto_path(const ConvParams& p, int dtype, bool al16 = true) {
   if (p.kw >= 2 && 10 * (int64_t)p.ow * p.oh >= 7 * wpad * hpad && convfwd::slab_accepts(p, dtype))
     return CONVFWD_PATH_SLAB;
   if (p.kw >= 2 && convfwd::strip_accepts(p, dtype)) return CONVFWD_PATH_STRIP;
+  // Stride 2 along h and w with 64-channel chunks: the stride-phase staging.
+  if (convfwd::phase_accepts(p, dtype)) return CONVFWD_PATH_PHASE;
   if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;
   if (convfwd::runs_accepts(p, dtype)) return CONVFWD_PATH_RUNS;
@@ -193,6 +196,7 @@ bool path_accepts(int path, const ConvParams& p, int dtype) {
     case CONVFWD_PATH_RUNS: return convfwd::runs_accepts(p, dtype);
     case CONVFWD_PATH_GROUPED: return convfwd::grouped_accepts(p, dtype);
     case CONVFWD_PATH_SLAB: return convfwd::slab_accepts(p, dtype);
+    case CONVFWD_PATH_PHASE: return convfwd::phase_accepts(p, dtype);
     default: return false;
   }
 }
@@ -208,6 +212,7 @@ hipError_t launch_path(int path, const ConvParams& p, int dtype, const void* x, 
     case CONVFWD_PATH_RUNS: return convfwd::launch_runs(p, dtype, x, w, y, s);
     case CONVFWD_PATH_GROUPED: return convfwd::launch_grouped(p, dtype, x, w, y, s);
     case CONVFWD_PATH_SLAB: return convfwd::launch_slab(p, dtype, x, w, y, s);
+    case CONVFWD_PATH_PHASE: return convfwd::launch_phase(p, dtype, x, w, y, s);
     default: return convfwd::launch_direct(p, dtype, x, w, y, s);
   }
 }
@@ -336,8 +341,8 @@ int run_tune(const convfwd_desc_ex* desc, const void* x, const void* w, void* y,
   const bool al16 = aligned_to(x, w, y, 16);
   Choice cand[64];
   int nc = 0;
-  const int paths[] = {CONVFWD_PATH_SLAB, CONVFWD_PATH_STRIP, CONVFWD_PATH_GROUPED, CONVFWD_PATH_ROWS,
-                       CONVFWD_PATH_RUNS, CONVFWD_PATH_FLATK, CONVFWD_PATH_BRICK};
+  const int paths[] = {CONVFWD_PATH_SLAB, CONVFWD_PATH_STRIP, CONVFWD_PATH_PHASE, CONVFWD_PATH_GROUPED,
+                       CONVFWD_PATH_ROWS, CONVFWD_PATH_RUNS, CONVFWD_PATH_FLATK, CONVFWD_PATH_BRICK};
   for (int q : paths)
     if (path_accepts(q, p, desc->dtype) && (al16 || !needs_16(q))) cand[nc++] = Choice{q, 0, 0.f};
   int ncfg = 0;
@@ -674,7 +679,7 @@ int conv_fwd_ex(const convfwd_desc_ex* desc, const void* x, const void* w, void*
 
 int conv_fwd_path_ex(const convfwd_desc_ex* desc, int path, const void* x, const void* w, void* y,
                      void* stream) {
-  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_SLAB) return CONVFWD_ERR_UNSUPPORTED;
+  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_PHASE) return CONVFWD_ERR_UNSUPPORTED;
   return run(desc, path, x, w, y, stream);
 }
 
@@ -729,6 +734,7 @@ const char* conv_path_name(int path) {
     case CONVFWD_PATH_RUNS: return "runs";
     case CONVFWD_PATH_GROUPED: return "grouped";
     case CONVFWD_PATH_SLAB: return "slab";
+    case CONVFWD_PATH_PHASE: return "phase";
     default: return "unknown";
   }
 }

@@ -102,7 +102,7 @@ typedef enum {
   CONVFWD_PATH_GROUPED = 8, /* any dtype, G > 1 with C_in/G in {1, 2, 4, 8, 16}, C_out/G <= 16 and
                               C_out * K_d*K_h*K_w * C_in/G <= 16384 (depthwise and small groups):
                               one thread per (output position, group), fp32 FMA, filter in LDS */
-  CONVFWD_PATH_SLAB = 9    /* fp16/bf16, C_in/G % 32 == 0, C_out % 4 == 0, G = 1 or C_out/G % 64 == 0,
+  CONVFWD_PATH_SLAB = 9,   /* fp16/bf16, C_in/G % 32 == 0, C_out % 4 == 0, G = 1 or C_out/G % 64 == 0,
                               stride 1 along h and w, K_h in {2, 3}, K_w <= 3, K_d <= 16,
                               dilation 1 along h and w or 2 along both with K_h = K_w = 3:
                               tiles of 16 output rows x 32 outputs (ragged at the ends) x 128
@@ -111,6 +111,13 @@ typedef enum {
                               units); per (channel chunk, kd) the input rows those windows
                               cover (18, dilated 20) are staged in LDS once and all K_h * K_w
                               taps read from them, MFMA */
+  CONVFWD_PATH_PHASE = 10  /* fp16/bf16, C_in/G % 64 == 0, C_out % 4 == 0, G = 1 or C_out/G % 64 == 0,
+                              stride 2 along h and w, K_h and K_w in {2, 3}, dilation 1 along h and
+                              w, K_d <= 16: tiles of 8 output rows x 16 outputs (ragged at the
+                              ends) x 64 channels; per (64-channel chunk, kd) the input rows the
+                              windows cover are staged in LDS split by stride phase (even rows and
+                              odd rows, each row's even positions before its odd ones), so every
+                              tap reads consecutive slots, MFMA */
 } convfwd_path;
 
 /* Problem descriptor.  All extents in elements. */
@@ -151,8 +158,8 @@ int conv_select_path(const convfwd_desc* desc);
 /* y = conv(x, w) on `stream` (a hipStream_t; NULL means the null stream of the
  * current device).  x, w, y are device pointers on the current device, laid
  * out as above, each aligned to its element size (2 bytes for fp16/bf16, 4 for
- * fp32; else CONVFWD_ERR_MISALIGNED).  The fast paths (slab, strip, main,
- * brick, rows, flatk) move 16-byte pieces counted from the base pointers and
+ * fp32; else CONVFWD_ERR_MISALIGNED).  The fast paths (slab, phase, strip,
+ * main, brick, rows, flatk) move 16-byte pieces counted from the base pointers and
  * need x, w and y all 16-byte aligned: with a tensor that is not, AUTO takes
  * the unaligned-channel tail path (runs) or, if that cannot take the
  * problem, direct, and a forced 16-byte path returns CONVFWD_ERR_UNSUPPORTED
@@ -248,8 +255,7 @@ int conv_bwd_data_path_ex(const convfwd_desc_ex* desc, int path, const void* dy,
 const char* conv_strerror(int code);
 
 /* Static name of a path ("auto", "main", "flatk", "rows", "direct", "brick", "strip", "runs",
- * "grouped", "slab");
- * never NULL. */
+ * "grouped", "slab", "phase"); never NULL. */
 const char* conv_path_name(int path);
 
 #ifdef __cplusplus

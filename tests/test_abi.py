@@ -134,9 +134,9 @@ def test_strerror_and_path_names():
     lib = igc.lib()
     for code in range(-7, 1):
         assert lib.conv_strerror(code)
-    assert [lib.conv_path_name(i).decode() for i in range(10)] == ["auto", "main", "flatk", "rows",
+    assert [lib.conv_path_name(i).decode() for i in range(11)] == ["auto", "main", "flatk", "rows",
                                                                    "direct", "brick", "strip", "runs",
-                                                                   "grouped", "slab"]
+                                                                   "grouped", "slab", "phase"]
 
 
 EXPECTED_PATHS = {
@@ -144,7 +144,7 @@ EXPECTED_PATHS = {
     "c2_conv2d_fp16_n32_56c256_o256": "slab",
     "c4a_conv3d_fp16_n4_32c128_o128": "slab",
     "c4b_conv3d_fp16_n1_64c64_o128": "slab",
-    "c4c_conv3d_fp16_n4_32c64_o128_s2": "main",
+    "c4c_conv3d_fp16_n4_32c64_o128_s2": "phase",
     "c5a_conv3d_bf16_n4_32c65_o65": "runs",
     "c5b_conv3d_bf16_n4_16c21_o21": "runs",
     "c5c_conv3d_bf16_n4_32c64_o128_k311": "main",
@@ -345,6 +345,12 @@ def test_forced_16_byte_paths_refuse_tensors_not_16_byte_aligned():
         assert lib.conv_fwd_path(ctypes.byref(d0), path, x, w, y, None) == 0
     # the descriptor-only choice assumes aligned tensors
     assert lib.conv_select_path(ctypes.byref(d)) == 6   # strip: 6 of 16 slab rows would be used
+    # the stride-2 path likewise
+    d2 = _desc(n=1, d=4, h=12, w=32, c_in=64, c_out=64, s_h=2, s_w=2)
+    assert lib.conv_select_path(ctypes.byref(d2)) == 10
+    assert lib.conv_fwd_path(ctypes.byref(d2), 10, x, w + 2, y, None) == -3
+    assert lib.conv_fwd_path(ctypes.byref(_desc(n=0, d=4, h=12, w=32, c_in=64, c_out=64, s_h=2, s_w=2)),
+                             10, x, w, y, None) == 0
 
 
 def test_pointers_not_aligned_to_their_element_are_rejected():

@@ -44,6 +44,8 @@ CANARY = [
     ("slab", "fp16", (1, 3, 19, 37, 64), (68, 3, 3, 3, 64), (1, 1, 1), (1, 1, 1), 1),
     ("slab", "bf16", (1, 2, 21, 40, 128), (256, 3, 3, 3, 128), (1, 1, 1), (1, 1, 1), 1),
     ("strip", "fp16", (1, 3, 5, 32, 64), (72, 3, 3, 3, 64), (1, 2, 1), (1, 1, 1), 1),
+    ("phase", "fp16", (1, 3, 19, 37, 64), (68, 3, 3, 3, 64), (1, 2, 2), (1, 1, 1), 1),
+    ("phase", "bf16", (2, 21, 34, 128), (256, 3, 2, 128), (2, 2), (1, 0), 1),
     ("main", "fp16", (2, 5, 6, 7, 64), (68, 3, 3, 3, 64), (2, 2, 2), (1, 1, 1), 1),
     ("main", "bf16", (3, 7, 9, 11, 64), (132, 3, 1, 1, 64), (1, 1, 1), (1, 0, 0), 1),
     ("brick", "fp16", (2, 5, 6, 7, 32), (36, 3, 3, 3, 32), (1, 1, 1), (1, 1, 1), 1),
@@ -154,7 +156,7 @@ def test_element_aligned_tensors_fall_back(case):
         assert torch.equal(ym.view(torch.uint8) if dtype != "fp32" else ym.view(torch.int32),
                            ya.view(torch.uint8) if dtype != "fp32" else ya.view(torch.int32))
     aligned_path = igc.select_path(xs, ws, st, pd, DT[dtype], groups=g)
-    if aligned_path in ("slab", "strip", "main", "rows"):
+    if aligned_path in ("slab", "phase", "strip", "main", "rows"):
         with pytest.raises(igc.ConvError) as err:
             igc.conv_fwd(xm, wm, st, pd, out=ym, path=aligned_path, groups=g)
         assert err.value.code == -3
@@ -181,7 +183,8 @@ def test_bwd_data_element_aligned_dy_falls_back():
 PLAIN = [
     # name, dtype, x shape, w shape, stride, pad, groups, the path AUTO takes
     ("slab_c64", "fp16", (2, 4, 16, 30, 64), (128, 3, 3, 3, 64), (1, 1, 1), (1, 1, 1), 1, "slab"),
-    ("main_s2", "fp16", (2, 11, 12, 13, 64), (128, 3, 3, 3, 64), (2, 2, 2), (1, 1, 1), 1, "main"),
+    ("phase_s2", "fp16", (2, 11, 12, 13, 64), (128, 3, 3, 3, 64), (2, 2, 2), (1, 1, 1), 1, "phase"),
+    ("main_s221", "fp16", (2, 11, 12, 13, 64), (128, 3, 3, 3, 64), (2, 2, 1), (1, 1, 1), 1, "main"),
     ("runs_c21", "bf16", (3, 6, 7, 8, 21), (21, 3, 3, 3, 21), (1, 1, 1), (1, 1, 1), 1, "runs"),
     ("rows_stem", "fp16", (2, 30, 32, 3), (64, 7, 7, 3), (2, 2), (3, 3), 1, "rows"),
     ("runs_fp32", "fp32", (1, 8, 8, 8, 16), (32, 3, 3, 3, 16), (1, 1, 1), (1, 1, 1), 1, "runs"),

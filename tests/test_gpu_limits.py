@@ -73,8 +73,10 @@ CASES = [
      ((1, 1), (1, 1), (1, 1)), (1, 1, 1), 1, "slab"),
     ("strip_2d_k5_c256", "fp16", (1, 2047, 2048, 256), (64, 5, 5, 256), (1, 1), ((2, 2), (2, 2)),
      (1, 1), 1, "strip"),
-    ("main_2d_c256_s2", "bf16", (1, 2047, 2048, 256), (128, 3, 3, 256), (2, 2), ((1, 1), (1, 1)),
+    ("main_2d_c256_s12", "bf16", (1, 2047, 2048, 256), (128, 3, 3, 256), (1, 2), ((1, 1), (1, 1)),
      (1, 1), 1, "main"),
+    ("phase_2d_c256_s2", "fp16", (1, 2047, 2048, 256), (128, 3, 3, 256), (2, 2), ((1, 1), (1, 1)),
+     (1, 1), 1, "phase"),
     # unaligned channels: 2,138,046,464 bytes of input
     ("runs_2d_c255", "fp16", (1, 2047, 2048, 255), (8, 3, 3, 255), (1, 1), ((1, 1), (1, 1)),
      (1, 1), 1, "runs"),

@@ -63,8 +63,15 @@ CASES = [
     _case("slab_bf16_w9_narrow", "bf16", (1, 3, 5, 9, 32), (40, 2, 2, 3, 32), (1, 1, 1), (0, 0, 1), seed=29),
     # an odd filter element count (7 x 27): the rows path copies its filter in 16-byte pieces
     _case("rows_odd_filter_fp16", "fp16", (1, 9, 16, 3), (7, 3, 3, 3), (1, 1), (1, 1), seed=30),
+    # stride 2 along h and w: ragged h, w and C_out tiles, two 64-channel chunks, 2 x 2 filters
+    _case("phase_fp16_c128_o68_ragged", "fp16", (1, 5, 19, 37, 128), (68, 3, 3, 3, 128), (1, 2, 2), (1, 1, 1),
+          seed=31),
+    _case("phase_bf16_2d_s2", "bf16", (3, 29, 35, 64), (64, 3, 3, 64), (2, 2), (1, 1), seed=32),
+    _case("phase_fp16_2d_k2", "fp16", (2, 17, 18, 64), (72, 2, 2, 64), (2, 2), (0, 0), seed=33),
+    _case("phase_fp16_k233_pad0", "fp16", (1, 7, 16, 16, 64), (64, 2, 3, 3, 64), (2, 2, 2), (0, 0, 0), seed=34),
+    _case("phase_bf16_k32_o200", "bf16", (1, 4, 18, 23, 192), (200, 1, 3, 2, 192), (1, 2, 2), (0, 1, 1), seed=35),
 ]
-PATHS = ["slab", "strip", "main", "brick", "rows", "runs", "flatk", "direct"]
+PATHS = ["slab", "phase", "strip", "main", "brick", "rows", "runs", "flatk", "direct"]
 
 
 def _accepts(wl, path):
@@ -79,6 +86,9 @@ def _accepts(wl, path):
     if path == "slab":
         return (half and wl.x_shape[-1] % 32 == 0 and wl.stride[-1] == 1 and wl.stride[-2] == 1
                 and wl.w_shape[-2] <= 3 and wl.w_shape[-3] in (2, 3))
+    if path == "phase":
+        return (half and wl.x_shape[-1] % 64 == 0 and wl.stride[-1] == 2 and wl.stride[-2] == 2
+                and wl.w_shape[-2] in (2, 3) and wl.w_shape[-3] in (2, 3))
     if path == "brick":
         return half and wl.x_shape[-1] % 16 == 0 and taps >= 4
     if path == "rows":
@@ -186,6 +196,9 @@ EXACT = [
     ("direct", "fp16", (1, 5, 6, 7, 3), (3, 3, 3), (2, 2, 2), (1, 1, 1)),
     ("rows", "fp16", (1, 1, 19, 16, 3), (1, 7, 7), (1, 2, 2), (0, 3, 3)),
     ("rows", "bf16", (2, 5, 9, 8, 3), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
+    ("phase", "fp16", (2, 5, 17, 18, 64), (3, 3, 3), (1, 2, 2), (1, 1, 1)),
+    ("phase", "bf16", (1, 6, 19, 33, 128), (3, 2, 3), (2, 2, 2), (2, 0, 1)),
+    ("phase", "fp16", (1, 4, 20, 21, 64), (2, 2, 2), (1, 2, 2), (0, 1, 0)),
 ]
 
 
@@ -329,8 +342,12 @@ VARIANTS = [
      ((1, 2), (2, 1)), (2, 2), 1),
     ("dilated3d_fp16_e2_g2_sd2", "fp16", (1, 5, 18, 34, 128), (128, 2, 3, 3, 64), (2, 1, 1),
      ((1, 0), (2, 2), (2, 2)), (2, 2, 2), 2),
+    ("phase_g2_asympad_bf16", "bf16", (2, 6, 17, 19, 128), (128, 3, 3, 3, 64), (1, 2, 2),
+     ((1, 1), (0, 2), (2, 1)), (1, 1, 1), 2),
+    ("phase_depth_dilated_fp16", "fp16", (1, 9, 16, 18, 64), (64, 3, 3, 2, 64), (1, 2, 2),
+     ((2, 2), (1, 1), (0, 1)), (2, 1, 1), 1),
 ]
-VARIANT_PATHS = ["main", "slab", "strip", "runs", "grouped", "direct"]
+VARIANT_PATHS = ["main", "slab", "phase", "strip", "runs", "grouped", "direct"]
 
 
 def _v_accepts(v, path):
@@ -346,6 +363,10 @@ def _v_accepts(v, path):
         ow = (xs[-2] + pads[-1][0] + pads[-1][1] - dil[-1] * (ws[-2] - 1) - 1) // st[-1] + 1
         return (half and g == 1 and dil[-1] == 1 and xs[-1] % 32 == 0 and ws[0] % 4 == 0
                 and st[-1] == 1 and ow % 32 == 0 and ws[-2] <= 5)
+    if path == "phase":
+        return (half and (g == 1 or cout_g % 64 == 0) and dil[-1] == 1 and dil[-2] == 1
+                and cin_g % 64 == 0 and ws[0] % 4 == 0 and st[-1] == 2 and st[-2] == 2
+                and ws[-2] in (2, 3) and ws[-3] in (2, 3))
     if path == "slab":
         return (half and (g == 1 or cout_g % 64 == 0) and dil[-1] == dil[-2]
                 and (dil[-1] == 1 or (dil[-1] == 2 and ws[-2] == 3 and ws[-3] == 3))
