@@ -31,13 +31,17 @@
 // goes out after the barrier that ends step s.  LDS: 2 x 38 KB + 33 KB +
 // 2 x 24 KB = 157 KB.
 //
-// Four waves, one per SIMD: wave v owns output rows 2v, 2v+1 of the tile (32
-// GEMM rows) x all 64 channels, two v_mfma_f32_32x32x16 blocks (32
-// accumulator registers).  Fragment reads run one unit (a tap's two k slices)
-// ahead of the MFMAs.  LDS positions and filter rows are 128 bytes; their
-// 16-byte chunks are XOR-swizzled by bits 1..3 of the slot (the position's
-// index inside its phase sub-row, or the filter row), so 16 lanes reading 16
-// consecutive slots hit 16 distinct bank groups.
+// Eight waves, two per SIMD: wave (mb = v % 4, kp = v / 4) owns output rows
+// 2 mb, 2 mb + 1 of the tile (32 GEMM rows) x all 64 channels, on the k
+// slices 2 kp, 2 kp + 1 of each 64-channel chunk (two v_mfma_f32_32x32x16
+// blocks, 32 accumulators); the two waves of a row block add their partial
+// sums through LDS at the end.  With one wave per SIMD the K steps were bound
+// by LDS fragment reads (one wave cannot keep enough reads in flight) and by
+// the per-lane set-up, which now splits over twice the waves.  Fragment reads
+// run one unit (a tap's k slice) ahead of the MFMAs.  LDS positions and filter
+// rows are 128 bytes; their 16-byte chunks are XOR-swizzled by bits 1..3 of
+// the slot (the position's index inside its phase sub-row, or the filter
+// row), so 16 lanes reading 16 consecutive slots hit 16 distinct bank groups.
 #include <type_traits>
 
 #include "conv_device.h"
@@ -58,6 +62,7 @@ constexpr int kBN = 64;             // output channels per tile
 constexpr int kCK = 64;             // input channels per chunk (one 128-byte position)
 constexpr int kPosB = kCK * 2;      // bytes per staged position / filter row
 constexpr int kLdsBytes = 160 * 1024;
+constexpr int kWaves = 8;           // two per SIMD
 
 template <int KH, int KW>
 struct PhaseGeom {
@@ -68,16 +73,16 @@ struct PhaseGeom {
   static constexpr int RO = kTH + (KH - 2) / 2;   // rows of O (input rows 1, 3, ..)
   static constexpr int WE = (RE * SR + 7) / 8;    // 1-KB wave loads (8 positions) per E block
   static constexpr int WO = (RO * SR + 7) / 8;
-  static constexpr int LE = (WE + 3) / 4;         // per wave, at most
-  static constexpr int LO = (WO + 3) / 4;
+  static constexpr int LE = (WE + kWaves - 1) / kWaves;   // per wave, at most
+  static constexpr int LO = (WO + kWaves - 1) / kWaves;
   static constexpr int EBYTES = WE * 1024;
   static constexpr int OBYTES = WO * 1024;
-  static constexpr int FLOADS = KW * kBN * 8 / 64;   // filter wave loads per step (2 KW per wave)
+  static constexpr int FLOADS = KW * kBN * 8 / 64;   // filter wave loads per step
   static constexpr int FBYTES = KW * kBN * kPosB;
   static constexpr int O_BASE = 2 * EBYTES;
   static constexpr int F_BASE = O_BASE + OBYTES;
   static constexpr int BYTES = F_BASE + 2 * FBYTES;
-  static_assert(FLOADS % 4 == 0, "whole filter rounds");
+  static_assert(FLOADS % kWaves == 0, "whole filter rounds");
   static_assert(BYTES <= kLdsBytes, "LDS");
 };
 
@@ -132,7 +137,7 @@ __device__ __forceinline__ int div_small(int x) {
 }
 
 template <typename T, int KH, int KW>
-__global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const T* __restrict__ x,
+__global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvParams p, const T* __restrict__ x,
                                                             const T* __restrict__ w,
                                                             T* __restrict__ y, PhaseArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const 
   const uint32_t dmask = p.ed == 1 ? (((1u << min(p.kd, max(0, p.d - z0))) - 1u) & ~((1u << max(0, -z0)) - 1u))
                                    : dim_mask(z0, p.kd, p.d, p.ed);
 
-  // ---- block loaders: wave load i = 4 l + wave fills positions 8 i .. 8 i + 7
+  // ---- block loaders: wave load i = 8 l + wave fills positions 8 i .. 8 i + 7
   // of the block (eight lanes each, one 16-byte chunk per lane).  This lane's
   // byte offset at (kd, chunk) = 0 and its depth mask (0 outside the input or
   // past the block's end).  The set-up runs on every workgroup before its
@@ -180,13 +185,14 @@ __global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const 
   const int rowB = p.xs_h * 2, posB = p.xs_w * 2;
   const uint32_t ubase = (uint32_t)((img * p.xs_n + z0 * p.xs_d + y0 * p.xs_h + x0 * p.xs_w + cbase) * 2);
   const int lane_pos = 8 * wave + (lane >> 3);   // this lane's position in wave load l = 0
+  constexpr int kRound = 8 * kWaves;             // positions per round of wave loads
   // base[l]: byte offset at (kd, chunk) = 0; bit l of *inside: the position lies
   // inside the input along h and w (and inside the block)
   auto setup = [&](uint32_t* base, uint32_t* inside, int L, int R, int odd) __attribute__((always_inline)) {
     uint32_t bits = 0;
 #pragma unroll
     for (int l = 0; l < L; ++l) {
-      const int pos = lane_pos + 32 * l;
+      const int pos = lane_pos + kRound * l;
       const int b = div_small<G::SR>(pos), slot = pos - b * G::SR;
       const int ph = slot >= G::SE ? 1 : 0;
       const int s = slot - ph * G::SE;             // index inside the phase sub-row
@@ -201,15 +207,15 @@ __global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const 
   };
   uint32_t e_base[G::LE], o_base[G::LO], e_in, o_in;
 
-  // ---- filter loader: wave load i = 4 l + wave fills rows R = 8 i .. 8 i + 7
+  // ---- filter loader: wave load i = 8 l + wave fills rows R = 8 i .. 8 i + 7
   // (R = kw * 64 + n) of a stage ----
-  constexpr int FL = G::FLOADS / 4;
+  constexpr int FL = G::FLOADS / kWaves;
   uint32_t f_base[FL];
   auto setup_filter = [&]() __attribute__((always_inline)) {
     const unsigned K2 = (unsigned)p.K * 2, cin2 = (unsigned)p.cin_g * 2;
 #pragma unroll
     for (int l = 0; l < FL; ++l) {
-      const int R = (4 * l + wave) * 8 + (lane >> 3);
+      const int R = (kWaves * l + wave) * 8 + (lane >> 3);
       const int kw = R >> 6, n = R & 63;
       const int c = (lane & 7) ^ ((R >> 1) & 7);
       f_base[l] = n0 + n < n_end ? __umul24((unsigned)(n0 + n), K2) + __umul24((unsigned)kw, cin2) + c * 16
@@ -232,8 +238,8 @@ __global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const 
     const uint32_t xo = (uint32_t)((kd * p.ed * p.xs_d + ch * kCK) * 2);
 #pragma unroll
     for (int l = l0; l < l1; ++l) {
-      if (4 * l + wave < W) {   // wave-uniform: the last round may be partial
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(buf + (4 * l + wave) * 1024), 16,
+      if (kWaves * l + wave < W) {   // wave-uniform: the last round may be partial
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(buf + (kWaves * l + wave) * 1024), 16,
                                                  ((in >> l) & 1u) ? base[l] + xo : kOutOfRange, 0, 0, 0);
       }
     }
@@ -245,25 +251,29 @@ __global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const 
     char* fbuf = f_buf + st * G::FBYTES;
 #pragma unroll
     for (int l = 0; l < FL; ++l)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(fbuf + (4 * l + wave) * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(fbuf + (kWaves * l + wave) * 1024), 16,
                                                (f_base[l] + wo) | dead, 0, 0, 0);
   };
 
-  // ---- fragment addresses: lane (r = lane % 32: tile row 2 wave + r / 16,
+  // ---- fragment addresses: wave (mb = wave % 4, kp = wave / 4) owns tile rows
+  // 32 mb .. 32 mb + 31 and the k slices 2 kp, 2 kp + 1 (channels 32 kp ..
+  // 32 kp + 31 of the chunk); lane (r = lane % 32: tile row 2 mb + r / 16,
   // output j = r % 16; kg = lane / 32).  A: slot j + (kw >> 1) of the phase
-  // sub-row kw & 1 of block row 2 wave + r / 16 + (kh >> 1); B: filter row
+  // sub-row kw & 1 of block row 2 mb + r / 16 + (kh >> 1); B: filter row
   // kw * 64 + 32 nb + r. ----
+  const int mb = wave & 3, kp = wave >> 2;
   const int r32 = lane & 31, kg = lane >> 5;
-  int a_off[2][4], b_off[4];
+  int a_off[2][2], b_off[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int s = (r32 & 15) + e;
-      a_off[e][ks] = ((2 * wave + (r32 >> 4)) * G::SR + s) * kPosB + (((2 * ks + kg) ^ ((s >> 1) & 7)) * 16);
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int s = (r32 & 15) + e, ks = 2 * kp + t2;
+      a_off[e][t2] = ((2 * mb + (r32 >> 4)) * G::SR + s) * kPosB + (((2 * ks + kg) ^ ((s >> 1) & 7)) * 16);
     }
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) b_off[ks] = r32 * kPosB + (((2 * ks + kg) ^ ((r32 >> 1) & 7)) * 16);
+  for (int t2 = 0; t2 < 2; ++t2)
+    b_off[t2] = r32 * kPosB + (((2 * (2 * kp + t2) + kg) ^ ((r32 >> 1) & 7)) * 16);
 
   f32x16_t acc[2];
 #pragma unroll
@@ -271,25 +281,21 @@ __global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const 
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[nb][e] = 0.f;
 
-  // unit u = (tap kw = u / 2, k-half h = u % 2) of step kh on block `ab`, filter stage `sb`
-  V8 fa[2][2], fb[2][2][2];   // [register buffer][k slice] and [register buffer][k slice][nb]
-  auto read_unit = [&](V8(&A)[2], V8(&B)[2][2], const char* ab, const char* sb, auto khc, auto uc)
+  // unit u = (tap kw = u / 2, the wave's k slice u % 2) of step kh on block
+  // `ab`, filter stage `sb`; double-buffered by unit (an even number per step)
+  V8 fa[2], fb[2][2];   // [register buffer] and [register buffer][nb]
+  auto read_unit = [&](V8& A, V8(&B)[2], const char* ab, const char* sb, auto khc, auto uc)
       __attribute__((always_inline)) {
     constexpr int kh = decltype(khc)::value, u = decltype(uc)::value;
-    constexpr int kw = u >> 1, h = u & 1;
+    constexpr int kw = u >> 1, t2 = u & 1;
     constexpr int imm = ((kh >> 1) * G::SR + (kw & 1) * G::SE) * kPosB;
+    A = *(const V8*)(ab + a_off[kw >> 1][t2] + imm);
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      A[t2] = *(const V8*)(ab + a_off[kw >> 1][2 * h + t2] + imm);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) B[t2][nb] = *(const V8*)(sb + b_off[2 * h + t2] + (kw * kBN + nb * 32) * kPosB);
-    }
+    for (int nb = 0; nb < 2; ++nb) B[nb] = *(const V8*)(sb + b_off[t2] + (kw * kBN + nb * 32) * kPosB);
   };
-  auto mma_unit = [&](const V8(&A)[2], const V8(&B)[2][2]) __attribute__((always_inline)) {
+  auto mma_unit = [&](const V8& A, const V8(&B)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32x32x16(B[t2][nb], A[t2], acc[nb]);
+    for (int nb = 0; nb < 2; ++nb) acc[nb] = mfma32x32x16(B[nb], A, acc[nb]);
   };
 
   // One step: kh on block ab with filter stage sb.  While unit u's MFMAs run,
@@ -309,9 +315,9 @@ __global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const 
         pieces(uc);
         mma_unit(fa[cur], fb[cur]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
@@ -323,9 +329,9 @@ __global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const 
         next2();
         mma_unit(fa[cur], fb[cur]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
         }
@@ -337,8 +343,8 @@ __global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const 
   };
 
   // per-wave piece counts of E and O (the last round of wave loads may be partial)
-  const bool e_full = wave < G::WE - 4 * (G::LE - 1);
-  const bool o_full = wave < G::WO - 4 * (G::LO - 1);
+  const bool e_full = wave < G::WE - kWaves * (G::LE - 1);
+  const bool o_full = wave < G::WO - kWaves * (G::LO - 1);
 
   // (kd, chunk) after (kd, ch) in the walk, kd fastest
   auto advance = [&](int& kd, int& ch) __attribute__((always_inline)) {
@@ -443,30 +449,50 @@ __global__ __launch_bounds__(256, 1) void conv_phase_kernel(ConvParams p, const 
     period(NP - 1, std::true_type{});
   }
 
-  // ---- epilogue: the tile goes through LDS so each store writes whole 16-byte
-  // pieces of output rows.  Lane (r32, kg) holds tile row 32 wave + r32 and
-  // channels 32 nb + 8 q + 4 kg + i; a row is 128 bytes in LDS, its piece k at
-  // slot k ^ (row % 8). ----
+  // ---- epilogue.  The two waves of a row block hold partial sums over their
+  // k slices: the upper one (kp = 1) writes its fp32 partials to LDS (32
+  // rows x 64 channels, 8 KB per row block, 16-byte unit u of row r at slot
+  // u ^ (r % 16)), the lower one adds them, rounds once and stages the tile
+  // in LDS (128-byte rows, 16-byte piece k at slot k ^ (row % 8)) so each
+  // store writes whole 16-byte pieces of output rows.  Lane (r32, kg) holds
+  // row 32 mb + r32, channels 32 nb + 8 q + 4 kg + i. ----
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  char* const part = smem + mb * 8192;
+  char* const tileb = smem + 4 * 8192;
+  if (kp == 1) {
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = wave * 32 + r32;
-      const int k = nb * 4 + q;
-      union { T h[4]; uint2 u; } pk;
+      for (int q = 0; q < 4; ++q) {
+        const int u = nb * 8 + 2 * q + kg;
+        const f32x4_t v4 = {acc[nb][4 * q], acc[nb][4 * q + 1], acc[nb][4 * q + 2], acc[nb][4 * q + 3]};
+        *(f32x4_t*)(part + r32 * 256 + ((u ^ (r32 & 15)) * 16)) = v4;
+      }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (kp == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[nb][4 * q + i]);
-      *(uint2*)(smem + row * 128 + ((k ^ (row & 7)) * 16) + kg * 8) = pk.u;
-    }
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = nb * 8 + 2 * q + kg;
+        const f32x4_t o4 = *(const f32x4_t*)(part + r32 * 256 + ((u ^ (r32 & 15)) * 16));
+        const int row = mb * 32 + r32;
+        const int k = nb * 4 + q;
+        union { T h[4]; uint2 u; } pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[nb][4 * q + i] + o4[i]);
+        *(uint2*)(tileb + row * 128 + ((k ^ (row & 7)) * 16) + kg * 8) = pk.u;
+      }
+  }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const bool whole16 = (p.cout & 7) == 0;
   const int64_t plane = (int64_t)(img * p.od + od) * p.oh;
 #pragma unroll
-  for (int it = 0; it < kBM * 8 / 256; ++it) {
-    const int piece = it * 256 + tid;
+  for (int it = 0; it < kBM * 8 / (64 * kWaves); ++it) {
+    const int piece = it * 64 * kWaves + tid;
     const int row = piece >> 3, k = piece & 7;
-    const uint4 v = *(const uint4*)(smem + row * 128 + ((k ^ (row & 7)) * 16));
+    const uint4 v = *(const uint4*)(tileb + row * 128 + ((k ^ (row & 7)) * 16));
     const int oh = oh0 + (row >> 4), ow = ow0 + (row & 15);
     const int n = n0 + k * 8;
     if (oh < p.oh && ow < p.ow) {
@@ -499,7 +525,7 @@ hipError_t launch_k(const ConvParams& p, const void* x, const void* w, void* y, 
   a.x_bytes = (uint32_t)((int64_t)p.n * p.xs_n * 2);
   a.w_bytes = (uint32_t)((int64_t)p.cout * p.K * 2);
   const int64_t tiles = (int64_t)p.n * p.od * a.hblocks * a.wblocks * a.tiles_n;
-  hipLaunchKernelGGL((conv_phase_kernel<T, KH, KW>), dim3((unsigned)tiles), dim3(256), 0, s, p, (const T*)x,
+  hipLaunchKernelGGL((conv_phase_kernel<T, KH, KW>), dim3((unsigned)tiles), dim3(64 * kWaves), 0, s, p, (const T*)x,
                      (const T*)w, (T*)y, a);
   return hipGetLastError();
 }
