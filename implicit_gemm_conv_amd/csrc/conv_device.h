@@ -101,6 +101,46 @@ __device__ __forceinline__ void store16_nt(void* dst, uint4 v) {
   store16_nt(dst, vv);
 }
 
+// ---- tile decode and small divisions without division sequences ----
+// The per-tile and per-lane set-up runs before a workgroup's first loads, and
+// with one or two waves per SIMD every instruction of it is exposed; a
+// division by a run-time value costs ~30 instructions, a quarter-rate 32-bit
+// multiply four times a full-rate one.
+
+// Tile grid of the staged kernels and, for each divisor of the tile decode,
+// m = ceil(2^32 / d) (0 for d = 1), computed on the host.
+struct TileArgs {
+  int tiles_n, wblocks, hblocks;
+  uint32_t m_tn, m_wb, m_hb, m_od;
+  uint32_t x_bytes, w_bytes;
+};
+
+inline uint32_t div_magic(int d) { return d <= 1 ? 0u : (uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d); }
+
+// floor(n / d) for 0 <= n < 2^24 with m = div_magic(d): n * m / 2^32 exceeds
+// n / d by less than 2^-8, so it is the quotient or one more.
+__device__ __forceinline__ int fast_div(int n, int d, uint32_t m) {
+  if (m == 0u) return n;
+  const int q = (int)__umulhi((uint32_t)n, m);
+  return q * d > n ? q - 1 : q;
+}
+
+// floor(x / D) for 0 <= x < 1024 with one full-rate 24-bit multiply: the
+// reciprocal rounded up errs by less than x * D / 2^16 / D < 1/64 of a unit,
+// while x / D lies at least 1/D below the next whole number.
+template <int D>
+__device__ __forceinline__ int div_small(int x) {
+  static_assert(D >= 1 && D <= 64, "small divisor");
+  return (int)(__umul24((unsigned)x, (65536u + D - 1) / D) >> 16);
+}
+
+// Depth taps t < k with 0 <= z0 + t * e < d, as dim_mask, without a division
+// when e == 1.
+__device__ __forceinline__ uint32_t depth_mask(int z0, int k, int d, int e) {
+  if (e == 1) return ((1u << min(k, max(0, d - z0))) - 1u) & ~((1u << max(0, -z0)) - 1u);
+  return dim_mask(z0, k, d, e);
+}
+
 // ---- XCD-aware tile order ----
 // Workgroups are dealt round-robin to the 8 XCDs (block b runs on XCD b % 8).
 // Give each XCD one contiguous run of tile ids so that the tiles resident on

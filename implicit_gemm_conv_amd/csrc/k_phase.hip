@@ -107,39 +107,10 @@ __host__ __device__ constexpr int step_kh(int i) {
   return KH == 3 ? (i == 0 ? 0 : i == 1 ? 2 : 1) : i;
 }
 
-// Launch constants computed on the host: the tile grid and, for each divisor
-// the tile decode needs, m = ceil(2^32 / d) (0 for d = 1), so that the decode
-// takes a multiply and a compare instead of a division sequence.
-struct PhaseArgs {
-  int tiles_n, wblocks, hblocks;
-  uint32_t m_tn, m_wb, m_hb, m_od;
-  uint32_t x_bytes, w_bytes;
-};
-
-inline uint32_t div_magic(int d) { return d <= 1 ? 0u : (uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d); }
-
-// floor(n / d) for 0 <= n < 2^24 with m = div_magic(d): n * m / 2^32 exceeds
-// n / d by less than 2^-8, so it is the quotient or one more.
-__device__ __forceinline__ int fast_div(int n, int d, uint32_t m) {
-  if (m == 0u) return n;
-  const int q = (int)__umulhi((uint32_t)n, m);
-  return q * d > n ? q - 1 : q;
-}
-
-// floor(x / D) for 0 <= x < 1024 with one full-rate 24-bit multiply (the
-// compiler's division by a constant uses a quarter-rate 32-bit one): the
-// reciprocal rounded up errs by less than x * D / 2^16 / D < 1/64 of a unit,
-// while x / D lies at least 1/D below the next whole number.
-template <int D>
-__device__ __forceinline__ int div_small(int x) {
-  static_assert(D >= 1 && D <= 64, "small divisor");
-  return (int)(__umul24((unsigned)x, (65536u + D - 1) / D) >> 16);
-}
-
 template <typename T, int KH, int KW>
 __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvParams p, const T* __restrict__ x,
                                                             const T* __restrict__ w,
-                                                            T* __restrict__ y, PhaseArgs a) {
+                                                            T* __restrict__ y, TileArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef typename Vec8<T>::type V8;
   typedef PhaseGeom<KH, KW> G;
@@ -172,8 +143,7 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvParams p, const 
   const __amdgpu_buffer_rsrc_t wr =
       __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, (int)a.w_bytes, kRawBufferFlags);
   // depth taps inside the input; without depth dilation no division is needed
-  const uint32_t dmask = p.ed == 1 ? (((1u << min(p.kd, max(0, p.d - z0))) - 1u) & ~((1u << max(0, -z0)) - 1u))
-                                   : dim_mask(z0, p.kd, p.d, p.ed);
+  const uint32_t dmask = depth_mask(z0, p.kd, p.d, p.ed);
 
   // ---- block loaders: wave load i = 8 l + wave fills positions 8 i .. 8 i + 7
   // of the block (eight lanes each, one 16-byte chunk per lane).  This lane's
@@ -514,7 +484,7 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvParams p, const 
 
 template <typename T, int KH, int KW>
 hipError_t launch_k(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
-  PhaseArgs a;
+  TileArgs a;
   a.tiles_n = (p.cout + kBN - 1) / kBN;
   a.wblocks = (p.ow + kTW - 1) / kTW;
   a.hblocks = (p.oh + kTH - 1) / kTH;

@@ -97,8 +97,7 @@ __device__ __forceinline__ int swz(int o, int c) { return c ^ ((o >> 2) & 3); }
 template <typename T, int KW, int KH, int NB, int E>
 __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T* __restrict__ x,
                                                            const T* __restrict__ w,
-                                                           T* __restrict__ y, int tiles_n,
-                                                           uint32_t x_bytes, uint32_t w_bytes) {
+                                                           T* __restrict__ y, TileArgs ta) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef typename Vec8<T>::type V8;
   static_assert(NB == 128 || NB == 64, "channels per tile");
@@ -130,60 +129,62 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
   // NB = 64: output rows 2 v .. 2 v + 1, all 64 channels
   const int wm = NB == 128 ? (wave & 3) : wave, wn = NB == 128 ? (wave >> 2) : 0;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int n0 = (tile % tiles_n) * NB;
+  // tile: column tiles fastest, then w-block, h-block, depth, image (the
+  // divisions by host-computed reciprocals)
+  int t = fast_div(tile, ta.tiles_n, ta.m_tn);
+  const int n0 = (tile - t * ta.tiles_n) * NB;
   // a column tile never straddles a channel group (NB divides C_out/G when
   // G > 1): the group's input channels start at cbase, its outputs end at n_end
-  const int grp = n0 / p.cout_g;
+  const int grp = p.groups == 1 ? 0 : n0 / p.cout_g;
   const int cbase = grp * p.cin_g, n_end = (grp + 1) * p.cout_g;
-  // tile rows: w-block fastest, then h-block, depth, image
-  const int wblocks = (p.ow + kSeg - 1) / kSeg, hblocks = (p.oh + kRowsOut - 1) / kRowsOut;
-  int t = tile / tiles_n;
-  const int ow0 = (t % wblocks) * kSeg;
-  t /= wblocks;
-  const int oh0 = (t % hblocks) * kRowsOut;
-  t /= hblocks;
-  const int od = t % p.od;
-  const int img = t / p.od;
+  int t2 = fast_div(t, ta.wblocks, ta.m_wb);
+  const int ow0 = (t - t2 * ta.wblocks) * kSeg;
+  t = fast_div(t2, ta.hblocks, ta.m_hb);
+  const int oh0 = (t2 - t * ta.hblocks) * kRowsOut;
+  const int img = fast_div(t, p.od, ta.m_od);
+  const int od = t - img * p.od;
   const int z0 = od * p.sd - p.pd;
   const int y0 = oh0 - p.ph;   // unit stride along h and w
   const int x0 = ow0 - p.pw;
 
   const __amdgpu_buffer_rsrc_t xr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)x_bytes, kRawBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)ta.x_bytes, kRawBufferFlags);
   const __amdgpu_buffer_rsrc_t wr =
-      __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, (int)w_bytes, kRawBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)w, (short)0, (int)ta.w_bytes, kRawBufferFlags);
 
   // ---- slab loader: wave load i = 8 q + wave fills positions 16 i .. 16 i + 15
   // (four lanes each, one 16-byte chunk per lane); this lane's row, position
   // and chunk.  Validity along h and w is fixed per lane; along depth it is a
   // bit mask over kd. ----
+  // (set-up with full-rate arithmetic only: 24-bit multiplies, a row of x and
+  // a filter row being under 2^24 bytes, which slab_accepts checks; selects)
   uint32_t a_base[kA_LOADS];   // byte offset of the piece at (kd, chunk) = 0
   uint32_t a_mask[kA_LOADS];   // depth bits; 0 if the position is outside the input or the slab
-  const uint32_t dmask = dim_mask(z0, p.kd, p.d, p.ed);
+  const uint32_t dmask = depth_mask(z0, p.kd, p.d, p.ed);
+  const uint32_t ubase = (uint32_t)((img * p.xs_n + z0 * p.xs_d + y0 * p.xs_h + x0 * p.xs_w + cbase) * 2);
+  const unsigned rowB = (unsigned)p.xs_h * 2, posB = (unsigned)p.xs_w * 2;
 #pragma unroll
   for (int q = 0; q < kA_LOADS; ++q) {
     const int pos = (8 * q + wave) * 16 + (lane >> 2);
-    const int r = pos / kSW, o = pos - (pos / kSW) * kSW;
+    const int r = div_small<kSW>(pos), o = pos - r * kSW;
     const int c = swz(o, lane & 3);                    // logical chunk this lane fetches
-    const int ih = y0 + r, iw = x0 + o;
-    uint32_t base = 0, mask = 0;
-    if (r < kRowsOut + (KH - 1) * E && o < kSeg + (KW - 1) * E && ih >= 0 && ih < p.h && iw >= 0 && iw < p.w) {
-      mask = dmask;
-      base = (uint32_t)(((img * p.xs_n + z0 * p.xs_d + ih * p.xs_h + iw * p.xs_w) + cbase + c * 8) * 2);
-    }
-    a_base[q] = base;
-    a_mask[q] = mask;
+    const bool ok = r < kRowsOut + (KH - 1) * E && o < kSeg + (KW - 1) * E &&
+                    (unsigned)(y0 + r) < (unsigned)p.h && (unsigned)(x0 + o) < (unsigned)p.w;
+    a_base[q] = ubase + __umul24((unsigned)r, rowB) + __umul24((unsigned)o, posB) + c * 16;
+    a_mask[q] = ok ? dmask : 0u;
   }
   // ---- filter loader: piece j = 512 s + tid -> (tap kw, row n, physical chunk) ----
   uint32_t b_base[B_LOADS];
+  const unsigned K2 = (unsigned)p.K * 2, cin2 = (unsigned)p.cin_g * 2;
 #pragma unroll
   for (int s = 0; s < B_LOADS; ++s) {
     const int j = s * 512 + tid;
     const int row = j >> 2, phys = j & 3;     // row = kw * NB + n
     const int kw = row / NB, n = row % NB;
     const int c = swz(row, phys);
-    b_base[s] = j < B_PIECES && (n0 + n) < n_end ? (uint32_t)(((n0 + n) * p.K + kw * p.cin_g + c * 8) * 2)
-                                                 : kOutOfRange;
+    b_base[s] = j < B_PIECES && (n0 + n) < n_end
+                    ? __umul24((unsigned)(n0 + n), K2) + __umul24((unsigned)kw, cin2) + c * 16
+                    : kOutOfRange;
   }
 
   const int nchunks = p.cin_g / 32;
@@ -406,11 +407,18 @@ __global__ __launch_bounds__(512, 1) void conv_slab_kernel(ConvParams p, const T
 template <typename T, int KW, int KH, int NB, int E>
 hipError_t launch_k(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   const int tiles_m = p.n * p.od * ((p.oh + kRowsOut - 1) / kRowsOut) * ((p.ow + kSeg - 1) / kSeg);
-  const int tiles_n = (p.cout + NB - 1) / NB;
-  const uint32_t xb = (uint32_t)((int64_t)p.n * p.xs_n * 2);
-  const uint32_t wb = (uint32_t)((int64_t)p.cout * p.K * 2);
-  hipLaunchKernelGGL((conv_slab_kernel<T, KW, KH, NB, E>), dim3(tiles_m * tiles_n), dim3(512), 0, s, p,
-                     (const T*)x, (const T*)w, (T*)y, tiles_n, xb, wb);
+  TileArgs ta;
+  ta.tiles_n = (p.cout + NB - 1) / NB;
+  ta.wblocks = (p.ow + kSeg - 1) / kSeg;
+  ta.hblocks = (p.oh + kRowsOut - 1) / kRowsOut;
+  ta.m_tn = div_magic(ta.tiles_n);
+  ta.m_wb = div_magic(ta.wblocks);
+  ta.m_hb = div_magic(ta.hblocks);
+  ta.m_od = div_magic(p.od);
+  ta.x_bytes = (uint32_t)((int64_t)p.n * p.xs_n * 2);
+  ta.w_bytes = (uint32_t)((int64_t)p.cout * p.K * 2);
+  hipLaunchKernelGGL((conv_slab_kernel<T, KW, KH, NB, E>), dim3(tiles_m * ta.tiles_n), dim3(512), 0, s, p,
+                     (const T*)x, (const T*)w, (T*)y, ta);
   return hipGetLastError();
 }
 
@@ -448,7 +456,11 @@ bool slab_accepts(const ConvParams& p, int dtype) {
   return (dtype == kF16 || dtype == kBF16) && p.remap == 0 && p.sh == 1 && p.sw == 1 &&
          p.eh == p.ew && (p.eh == 1 || (p.eh == 2 && p.kh == 3 && p.kw == 3)) && p.cin_g % 32 == 0 && p.cout % 4 == 0 &&
          (p.groups == 1 || p.cout_g % 64 == 0) &&
-         p.kw <= kMaxKW && p.kh >= 2 && p.kh <= kMaxKH && p.kd <= 16;
+         p.kw <= kMaxKW && p.kh >= 2 && p.kh <= kMaxKH && p.kd <= 16 &&
+         // the set-up's 24-bit multiplies and tile decode
+         (int64_t)p.xs_h * 2 < (1 << 24) && (int64_t)p.K * 2 < (1 << 24) &&
+         (int64_t)p.n * p.od * ((p.oh + kRowsOut - 1) / kRowsOut) * ((p.ow + kSeg - 1) / kSeg) *
+                 ((p.cout + 63) / 64) < (1 << 24);
 }
 
 hipError_t launch_slab(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
