@@ -17,7 +17,7 @@ import torch
 from .build import LIB as _LIB_PATH
 
 PATHS = {"auto": 0, "main": 1, "flatk": 2, "rows": 3, "direct": 4, "brick": 5, "strip": 6, "runs": 7,
-         "grouped": 8, "slab": 9, "phase": 10}
+         "grouped": 8, "slab": 9, "phase": 10, "staged": 11}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 _DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 

@@ -60,6 +60,8 @@ hipError_t launch_slab(const ConvParams& p, int dtype, const void* x, const void
                        hipStream_t s);
 hipError_t launch_phase(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
                         hipStream_t s);
+hipError_t launch_staged(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
+                         hipStream_t s);
 
 // Backward-data filter rearrangement (see k_bwd.hip): per dimension the stride
 // s, dilation e, low pad p, filter extent K and, per stride phase r < s, the
@@ -95,6 +97,7 @@ bool runs_accepts(const ConvParams& p, int dtype);
 bool grouped_accepts(const ConvParams& p, int dtype);
 bool slab_accepts(const ConvParams& p, int dtype);
 bool phase_accepts(const ConvParams& p, int dtype);
+bool staged_accepts(const ConvParams& p, int dtype);
 
 // Compute units of the current device (looked up once per device).
 int device_cus();

@@ -161,26 +161,33 @@ bool aligned_to(const void* a, const void* b, const void* c, uintptr_t bytes) {
 // The brick path is available on request; on the measured shapes the
 // per-tap-gather main path is faster, so AUTO does not pick it.  With tensors
 // that are not all 16-byte aligned AUTO keeps to the paths that need element
-// alignment only (the unaligned-channel tail path, else direct), the
-// fall-back-rather-than-fail rule of the MLX pull request's dispatch.
+// alignment only (staged, runs, else direct), the fall-back-rather-than-fail
+// rule of the MLX pull request's dispatch.
 int auto_path(const ConvParams& p, int dtype, bool al16 = true) {
   // Few channels per group (down to depthwise): the memory-bound vector-ALU form.
   if (convfwd::grouped_accepts(p, dtype)) return CONVFWD_PATH_GROUPED;
-  if (!al16) return convfwd::runs_accepts(p, dtype) ? CONVFWD_PATH_RUNS : CONVFWD_PATH_DIRECT;
+  // The slab and staged paths compute whole blocks of 16 rows x 32 outputs;
+  // they are taken when at least 70% of that area lies inside the output (on
+  // (32,56^2,256) with 77% the slab path runs 1.17x faster than the main path).
+  const int64_t wpad = (p.ow + 31) / 32 * 32, hpad = (p.oh + 15) / 16 * 16;
+  const bool blocks_fit = 10 * (int64_t)p.ow * p.oh >= 7 * wpad * hpad;
+  const bool staged = blocks_fit && convfwd::staged_accepts(p, dtype);
+  if (!al16) {
+    if (staged) return CONVFWD_PATH_STAGED;
+    return convfwd::runs_accepts(p, dtype) ? CONVFWD_PATH_RUNS : CONVFWD_PATH_DIRECT;
+  }
   // Once the w-taps share a strip (K_w >= 2): the slab path where the h-taps
   // share its staged rows too, else the strip path.  With K_w = 1 the strip
   // path is the main path with a larger tile and the main path is faster.
-  // The slab path computes whole blocks of 16 rows x 32 outputs; it is taken
-  // when at least 70% of that area lies inside the output (on (32,56^2,256)
-  // with 77% it runs 1.17x faster than the main path).
-  const int64_t wpad = (p.ow + 31) / 32 * 32, hpad = (p.oh + 15) / 16 * 16;
-  if (p.kw >= 2 && 10 * (int64_t)p.ow * p.oh >= 7 * wpad * hpad && convfwd::slab_accepts(p, dtype))
-    return CONVFWD_PATH_SLAB;
+  if (p.kw >= 2 && blocks_fit && convfwd::slab_accepts(p, dtype)) return CONVFWD_PATH_SLAB;
   if (p.kw >= 2 && convfwd::strip_accepts(p, dtype)) return CONVFWD_PATH_STRIP;
   // Stride 2 along h and w with 64-channel chunks: the stride-phase staging.
   if (convfwd::phase_accepts(p, dtype)) return CONVFWD_PATH_PHASE;
   if (convfwd::main_accepts(p, dtype)) return CONVFWD_PATH_MAIN;
   if (convfwd::rows_accepts(p, dtype)) return CONVFWD_PATH_ROWS;
+  // Channel counts the 16-byte paths cannot take (C_in = 65): the slab scheme
+  // staged through registers, else whole-window runs.
+  if (staged) return CONVFWD_PATH_STAGED;
   if (convfwd::runs_accepts(p, dtype)) return CONVFWD_PATH_RUNS;
   return CONVFWD_PATH_DIRECT;
 }
@@ -197,6 +204,7 @@ bool path_accepts(int path, const ConvParams& p, int dtype) {
     case CONVFWD_PATH_GROUPED: return convfwd::grouped_accepts(p, dtype);
     case CONVFWD_PATH_SLAB: return convfwd::slab_accepts(p, dtype);
     case CONVFWD_PATH_PHASE: return convfwd::phase_accepts(p, dtype);
+    case CONVFWD_PATH_STAGED: return convfwd::staged_accepts(p, dtype);
     default: return false;
   }
 }
@@ -213,6 +221,7 @@ hipError_t launch_path(int path, const ConvParams& p, int dtype, const void* x, 
     case CONVFWD_PATH_GROUPED: return convfwd::launch_grouped(p, dtype, x, w, y, s);
     case CONVFWD_PATH_SLAB: return convfwd::launch_slab(p, dtype, x, w, y, s);
     case CONVFWD_PATH_PHASE: return convfwd::launch_phase(p, dtype, x, w, y, s);
+    case CONVFWD_PATH_STAGED: return convfwd::launch_staged(p, dtype, x, w, y, s);
     default: return convfwd::launch_direct(p, dtype, x, w, y, s);
   }
 }
@@ -341,8 +350,9 @@ int run_tune(const convfwd_desc_ex* desc, const void* x, const void* w, void* y,
   const bool al16 = aligned_to(x, w, y, 16);
   Choice cand[64];
   int nc = 0;
-  const int paths[] = {CONVFWD_PATH_SLAB, CONVFWD_PATH_STRIP, CONVFWD_PATH_PHASE, CONVFWD_PATH_GROUPED,
-                       CONVFWD_PATH_ROWS, CONVFWD_PATH_RUNS, CONVFWD_PATH_FLATK, CONVFWD_PATH_BRICK};
+  const int paths[] = {CONVFWD_PATH_SLAB, CONVFWD_PATH_STRIP, CONVFWD_PATH_PHASE, CONVFWD_PATH_STAGED,
+                       CONVFWD_PATH_GROUPED, CONVFWD_PATH_ROWS, CONVFWD_PATH_RUNS, CONVFWD_PATH_FLATK,
+                       CONVFWD_PATH_BRICK};
   for (int q : paths)
     if (path_accepts(q, p, desc->dtype) && (al16 || !needs_16(q))) cand[nc++] = Choice{q, 0, 0.f};
   int ncfg = 0;
@@ -679,7 +689,7 @@ int conv_fwd_ex(const convfwd_desc_ex* desc, const void* x, const void* w, void*
 
 int conv_fwd_path_ex(const convfwd_desc_ex* desc, int path, const void* x, const void* w, void* y,
                      void* stream) {
-  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_PHASE) return CONVFWD_ERR_UNSUPPORTED;
+  if (path < CONVFWD_PATH_AUTO || path > CONVFWD_PATH_STAGED) return CONVFWD_ERR_UNSUPPORTED;
   return run(desc, path, x, w, y, stream);
 }
 
@@ -735,6 +745,7 @@ const char* conv_path_name(int path) {
     case CONVFWD_PATH_GROUPED: return "grouped";
     case CONVFWD_PATH_SLAB: return "slab";
     case CONVFWD_PATH_PHASE: return "phase";
+    case CONVFWD_PATH_STAGED: return "staged";
     default: return "unknown";
   }
 }

@@ -111,13 +111,21 @@ typedef enum {
                               units); per (channel chunk, kd) the input rows those windows
                               cover (18, dilated 20) are staged in LDS once and all K_h * K_w
                               taps read from them, MFMA */
-  CONVFWD_PATH_PHASE = 10  /* fp16/bf16, C_in/G % 64 == 0, C_out % 4 == 0, G = 1 or C_out/G % 64 == 0,
+  CONVFWD_PATH_PHASE = 10, /* fp16/bf16, C_in/G % 64 == 0, C_out % 4 == 0, G = 1 or C_out/G % 64 == 0,
                               stride 2 along h and w, K_h and K_w in {2, 3}, dilation 1 along h and
                               w, K_d <= 16: tiles of 8 output rows x 16 outputs (ragged at the
                               ends) x 64 channels; per (64-channel chunk, kd) the input rows the
                               windows cover are staged in LDS split by stride phase (even rows and
                               odd rows, each row's even positions before its odd ones), so every
                               tap reads consecutive slots, MFMA */
+  CONVFWD_PATH_STAGED = 11 /* fp16/bf16, G = 1, any C_in with (C_in % 8) * K_d*K_h*K_w <= 32, stride 1
+                              and dilation 1 along h and w, K_h and K_w in {2, 3}, K_d <= 16,
+                              element-aligned tensors suffice: the slab scheme with the input
+                              staged through registers (unaligned 16-byte loads, so positions of
+                              any channel count), tiles of 16 output rows x 32 outputs x 32, 64
+                              or 80 channels; channels below C_in - C_in % 8 walk the slab in
+                              32-channel chunks, the C_in % 8 left over are packed across all taps
+                              into one extra K block of 32, MFMA */
 } convfwd_path;
 
 /* Problem descriptor.  All extents in elements. */
@@ -160,9 +168,10 @@ int conv_select_path(const convfwd_desc* desc);
  * out as above, each aligned to its element size (2 bytes for fp16/bf16, 4 for
  * fp32; else CONVFWD_ERR_MISALIGNED).  The fast paths (slab, phase, strip,
  * main, brick, rows, flatk) move 16-byte pieces counted from the base pointers and
- * need x, w and y all 16-byte aligned: with a tensor that is not, AUTO takes
- * the unaligned-channel tail path (runs) or, if that cannot take the
- * problem, direct, and a forced 16-byte path returns CONVFWD_ERR_UNSUPPORTED
+ * need x, w and y all 16-byte aligned: with a tensor that is not, AUTO keeps to
+ * the paths that need element alignment only (staged, else runs, else direct;
+ * grouped checks its own 16-byte kernel), and a forced 16-byte path returns
+ * CONVFWD_ERR_UNSUPPORTED
  * (the MLX pull request's dispatch falls back rather than failing).  Tensors
  * from an allocator are 256-byte aligned; a view at an element offset may not
  * be.  Asynchronous: returns after the launch.  With N = 0 it launches nothing
@@ -255,7 +264,7 @@ int conv_bwd_data_path_ex(const convfwd_desc_ex* desc, int path, const void* dy,
 const char* conv_strerror(int code);
 
 /* Static name of a path ("auto", "main", "flatk", "rows", "direct", "brick", "strip", "runs",
- * "grouped", "slab", "phase"); never NULL. */
+ * "grouped", "slab", "phase", "staged"); never NULL. */
 const char* conv_path_name(int path);
 
 #ifdef __cplusplus

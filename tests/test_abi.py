@@ -134,9 +134,9 @@ def test_strerror_and_path_names():
     lib = igc.lib()
     for code in range(-7, 1):
         assert lib.conv_strerror(code)
-    assert [lib.conv_path_name(i).decode() for i in range(11)] == ["auto", "main", "flatk", "rows",
+    assert [lib.conv_path_name(i).decode() for i in range(12)] == ["auto", "main", "flatk", "rows",
                                                                    "direct", "brick", "strip", "runs",
-                                                                   "grouped", "slab", "phase"]
+                                                                   "grouped", "slab", "phase", "staged"]
 
 
 EXPECTED_PATHS = {
@@ -145,7 +145,7 @@ EXPECTED_PATHS = {
     "c4a_conv3d_fp16_n4_32c128_o128": "slab",
     "c4b_conv3d_fp16_n1_64c64_o128": "slab",
     "c4c_conv3d_fp16_n4_32c64_o128_s2": "phase",
-    "c5a_conv3d_bf16_n4_32c65_o65": "runs",
+    "c5a_conv3d_bf16_n4_32c65_o65": "staged",
     "c5b_conv3d_bf16_n4_16c21_o21": "runs",
     "c5c_conv3d_bf16_n4_32c64_o128_k311": "main",
     "c5d_conv3d_bf16_n4_32c64_o128_k133": "slab",

@@ -57,6 +57,9 @@ CANARY = [
     ("direct", "fp16", (1, 5, 6, 7, 3), (5, 3, 3, 3, 3), (2, 1, 2), (1, 1, 1), 1),
     ("grouped", "fp16", (2, 9, 10, 32), (32, 3, 3, 1), (1, 1), (1, 1), 32),
     ("grouped", "bf16", (2, 9, 10, 12), (18, 3, 3, 2), (1, 1), (1, 1), 6),
+    ("staged", "bf16", (1, 3, 19, 37, 65), (65, 3, 3, 3, 65), (1, 1, 1), (1, 1, 1), 1),
+    ("staged", "fp16", (2, 18, 40, 33), (130, 3, 2, 33), (1, 1), (1, 1), 1),
+    ("staged", "fp16", (1, 4, 16, 32, 1), (24, 3, 3, 3, 1), (1, 1, 1), (1, 1, 1), 1),
 ]
 
 
@@ -126,6 +129,8 @@ MISALIGNED = [
     ("tail_c21_y", "bf16", (2, 6, 7, 8, 21), (21, 3, 3, 3, 21), (1, 1, 1), (1, 1, 1), 1, "y"),
     ("fp32_x", "fp32", (1, 6, 6, 6, 16), (32, 3, 3, 3, 16), (1, 1, 1), (1, 1, 1), 1, "xy"),
     ("depthwise_x", "fp16", (2, 9, 10, 32), (32, 3, 3, 1), (1, 1), (1, 1), 32, "x"),
+    ("staged_c65_xwy", "bf16", (1, 3, 16, 32, 65), (65, 3, 3, 3, 65), (1, 1, 1), (1, 1, 1), 1, "xwy"),
+    ("staged_shape_c64_x", "fp16", (1, 3, 16, 32, 64), (64, 3, 3, 3, 64), (1, 1, 1), (1, 1, 1), 1, "x"),
 ]
 
 
@@ -133,7 +138,7 @@ MISALIGNED = [
 def test_element_aligned_tensors_fall_back(case):
     """x, w or y at an odd element offset (element-aligned, not 16-byte aligned): AUTO runs
     the problem on a path that needs element alignment only and matches the oracle; on the
-    tail path the result equals that path's result on aligned copies bit for bit (the same
+    fall-back path (staged or runs) the result equals that path's result on aligned copies bit for bit (the same
     kernel and summation order; the grouped path switches from its 16-byte kernel to its
     general one); a forced 16-byte path is refused before any launch."""
     name, dtype, xs, ws, st, pd, g, which = case
@@ -151,10 +156,17 @@ def test_element_aligned_tensors_fall_back(case):
     torch.cuda.synchronize()
     assert_parity(oracle.to_float64(ym), _ref(x, w, st, pd, groups=g), dtype, name)
     if g == 1:
-        ya = igc.conv_fwd(x, w, st, pd, path="runs")
-        torch.cuda.synchronize()
-        assert torch.equal(ym.view(torch.uint8) if dtype != "fp32" else ym.view(torch.int32),
-                           ya.view(torch.uint8) if dtype != "fp32" else ya.view(torch.int32))
+        # the element-aligned paths AUTO may fall back to: staged, else runs
+        bits = (lambda t: t.view(torch.uint8) if dtype != "fp32" else t.view(torch.int32))
+        same = []
+        for p in ("staged", "runs"):
+            try:
+                ya = igc.conv_fwd(x, w, st, pd, path=p)
+            except igc.ConvError:
+                continue
+            torch.cuda.synchronize()
+            same.append(torch.equal(bits(ym), bits(ya)))
+        assert any(same), same
     aligned_path = igc.select_path(xs, ws, st, pd, DT[dtype], groups=g)
     if aligned_path in ("slab", "phase", "strip", "main", "rows"):
         with pytest.raises(igc.ConvError) as err:
@@ -189,6 +201,7 @@ PLAIN = [
     ("rows_stem", "fp16", (2, 30, 32, 3), (64, 7, 7, 3), (2, 2), (3, 3), 1, "rows"),
     ("runs_fp32", "fp32", (1, 8, 8, 8, 16), (32, 3, 3, 3, 16), (1, 1, 1), (1, 1, 1), 1, "runs"),
     ("grouped_depthwise", "bf16", (2, 6, 7, 9, 32), (32, 3, 3, 3, 1), (1, 1, 1), (1, 1, 1), 32, "grouped"),
+    ("staged_c65", "bf16", (1, 4, 16, 32, 65), (65, 3, 3, 3, 65), (1, 1, 1), (1, 1, 1), 1, "staged"),
 ]
 
 

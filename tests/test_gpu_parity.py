@@ -70,8 +70,21 @@ CASES = [
     _case("phase_fp16_2d_k2", "fp16", (2, 17, 18, 64), (72, 2, 2, 64), (2, 2), (0, 0), seed=33),
     _case("phase_fp16_k233_pad0", "fp16", (1, 7, 16, 16, 64), (64, 2, 3, 3, 64), (2, 2, 2), (0, 0, 0), seed=34),
     _case("phase_bf16_k32_o200", "bf16", (1, 4, 18, 23, 192), (200, 1, 3, 2, 192), (1, 2, 2), (0, 1, 1), seed=35),
+    # C_in not a multiple of 8: 32-channel chunks plus the packed leftover block; ragged h and w
+    # blocks, 80-, 64- and 32-channel tiles, two column tiles (element-wise stores), pack only
+    _case("staged_bf16_c65_o65_ragged", "bf16", (1, 5, 19, 37, 65), (65, 3, 3, 3, 65), (1, 1, 1), (1, 1, 1),
+          seed=36),
+    _case("staged_fp16_c1_pack_only", "fp16", (2, 6, 20, 33, 1), (24, 3, 3, 3, 1), (1, 1, 1), (1, 1, 1), seed=37),
+    _case("staged_bf16_2d_c3_o40", "bf16", (3, 21, 40, 3), (40, 3, 3, 3), (1, 1), (1, 1), seed=38),
+    _case("staged_fp16_c40_partial_chunk", "fp16", (1, 4, 18, 34, 40), (33, 3, 3, 3, 40), (1, 1, 1), (1, 1, 1),
+          seed=39),
+    _case("staged_fp16_2d_c33_o130_kw2", "fp16", (2, 18, 35, 33), (130, 3, 2, 33), (1, 1), (1, 0), seed=40),
+    _case("staged_bf16_k223_c66_o70", "bf16", (1, 3, 17, 33, 66), (70, 2, 2, 3, 66), (1, 1, 1), (0, 1, 1),
+          seed=41),
+    _case("staged_fp16_2d_c24_o16", "fp16", (2, 16, 64, 24), (16, 3, 3, 24), (1, 1), (1, 1), seed=42),
+    _case("staged_bf16_sd2_c17_o48", "bf16", (2, 9, 16, 32, 17), (48, 3, 3, 3, 17), (2, 1, 1), (1, 1, 1), seed=43),
 ]
-PATHS = ["slab", "phase", "strip", "main", "brick", "rows", "runs", "flatk", "direct"]
+PATHS = ["slab", "phase", "staged", "strip", "main", "brick", "rows", "runs", "flatk", "direct"]
 
 
 def _accepts(wl, path):
@@ -89,6 +102,9 @@ def _accepts(wl, path):
     if path == "phase":
         return (half and wl.x_shape[-1] % 64 == 0 and wl.stride[-1] == 2 and wl.stride[-2] == 2
                 and wl.w_shape[-2] in (2, 3) and wl.w_shape[-3] in (2, 3))
+    if path == "staged":
+        return (wl.dtype in ("fp16", "bf16") and wl.stride[-1] == 1 and wl.stride[-2] == 1
+                and wl.w_shape[-2] in (2, 3) and wl.w_shape[-3] in (2, 3) and (wl.x_shape[-1] % 8) * taps <= 32)
     if path == "brick":
         return half and wl.x_shape[-1] % 16 == 0 and taps >= 4
     if path == "rows":
@@ -199,6 +215,10 @@ EXACT = [
     ("phase", "fp16", (2, 5, 17, 18, 64), (3, 3, 3), (1, 2, 2), (1, 1, 1)),
     ("phase", "bf16", (1, 6, 19, 33, 128), (3, 2, 3), (2, 2, 2), (2, 0, 1)),
     ("phase", "fp16", (1, 4, 20, 21, 64), (2, 2, 2), (1, 2, 2), (0, 1, 0)),
+    ("staged", "bf16", (1, 4, 17, 35, 65), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
+    ("staged", "fp16", (2, 3, 16, 33, 17), (3, 2, 3), (2, 1, 1), (1, 0, 2)),
+    ("staged", "fp16", (1, 2, 18, 32, 2), (2, 3, 2), (1, 1, 1), (1, 1, 0)),
+    ("staged", "bf16", (2, 17, 40, 40), (3, 3), (1, 1), (1, 1)),
 ]
 
 
@@ -220,13 +240,27 @@ def test_tap_count_bit_exact(path, dtype, xs, ks, st, pd):
     np.testing.assert_array_equal(oracle.to_float64(y), ref)
 
 
+@pytest.mark.parametrize("path,dtype,xs,ks,st,pd", [e for e in EXACT if e[2][-1] % 8])
+def test_tap_count_last_channel_bit_exact(path, dtype, xs, ks, st, pd):
+    """As above on the last input channel, the one past the last 8-channel piece (on the
+    staged path: packed with the other taps' leftover channels into one K block)."""
+    cin = xs[-1]
+    x = torch.ones(xs, dtype=_dt(dtype), device=DEV)
+    w = torch.zeros((8, *ks, cin), dtype=_dt(dtype), device=DEV)
+    w[..., cin - 1] = 1
+    y = igc.conv_fwd(x, w, st, pd, path=path)
+    torch.cuda.synchronize()
+    ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), st, pd)
+    np.testing.assert_array_equal(oracle.to_float64(y), ref)
+
+
 @pytest.mark.parametrize("path,dtype,xs,ks,st,pd", EXACT)
 def test_one_hot_gather_bit_exact(path, dtype, xs, ks, st, pd):
     """w = identity on channels at one tap: y is a shifted, strided copy of x (0 in the padding)."""
     c = xs[-1]
     g = torch.Generator("cpu").manual_seed(99)
     x = (torch.rand(xs, generator=g) * 2 - 1).to(_dt(dtype)).to(DEV)
-    taps = [(0, 0, 0), tuple(k - 1 for k in ks), tuple(k // 2 for k in ks)]
+    taps = [tuple(0 for _ in ks), tuple(k - 1 for k in ks), tuple(k // 2 for k in ks)]
     for tap in taps:
         w = torch.zeros((c, *ks, c), dtype=_dt(dtype))
         w[(torch.arange(c), *[torch.full((c,), t) for t in tap], torch.arange(c))] = 1
@@ -346,8 +380,12 @@ VARIANTS = [
      ((1, 1), (0, 2), (2, 1)), (1, 1, 1), 2),
     ("phase_depth_dilated_fp16", "fp16", (1, 9, 16, 18, 64), (64, 3, 3, 2, 64), (1, 2, 2),
      ((2, 2), (1, 1), (0, 1)), (2, 1, 1), 1),
+    ("staged_depth_dilated_bf16_c65", "bf16", (1, 9, 16, 33, 65), (48, 3, 3, 3, 65), (1, 1, 1),
+     ((2, 2), (1, 1), (1, 1)), (2, 1, 1), 1),
+    ("staged_asympad_sd2_fp16_c33", "fp16", (2, 5, 17, 40, 33), (70, 3, 2, 3, 33), (2, 1, 1),
+     ((1, 0), (0, 1), (2, 0)), (1, 1, 1), 1),
 ]
-VARIANT_PATHS = ["main", "slab", "phase", "strip", "runs", "grouped", "direct"]
+VARIANT_PATHS = ["main", "slab", "phase", "staged", "strip", "runs", "grouped", "direct"]
 
 
 def _v_accepts(v, path):
@@ -367,6 +405,9 @@ def _v_accepts(v, path):
         return (half and (g == 1 or cout_g % 64 == 0) and dil[-1] == 1 and dil[-2] == 1
                 and cin_g % 64 == 0 and ws[0] % 4 == 0 and st[-1] == 2 and st[-2] == 2
                 and ws[-2] in (2, 3) and ws[-3] in (2, 3))
+    if path == "staged":
+        return (half and g == 1 and dil[-1] == 1 and dil[-2] == 1 and st[-1] == 1 and st[-2] == 1
+                and ws[-2] in (2, 3) and ws[-3] in (2, 3) and (xs[-1] % 8) * int(np.prod(ws[1:-1])) <= 32)
     if path == "slab":
         return (half and (g == 1 or cout_g % 64 == 0) and dil[-1] == dil[-2]
                 and (dil[-1] == 1 or (dil[-1] == 2 and ws[-2] == 3 and ws[-3] == 3))

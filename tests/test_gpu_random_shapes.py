@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
-FWD_PATHS = ["auto", "main", "slab", "phase", "strip", "runs", "rows", "grouped", "flatk", "brick", "direct"]
+FWD_PATHS = ["auto", "main", "slab", "phase", "staged", "strip", "runs", "rows", "grouped", "flatk", "brick",
+             "direct"]
 
 
 def _macs(xs, ws, st, pads, dil, g):
