@@ -58,6 +58,8 @@ namespace convfwd {
 
 namespace {
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr int kRawBufferFlags = 0x00020000;
 
@@ -117,13 +119,20 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
   constexpr int B_PIECES = B_ROWS * 4;             // a multiple of 64
   constexpr int B_LOADS = (B_PIECES + kThreads - 1) / kThreads;
   constexpr int F_BASE = 2 * kSlabBytes;
-  constexpr int PK_A = F_BASE + 2 * B_BYTES;       // the packed block: input side
-  constexpr int PK_B = PK_A + kBM * 64;            //   and filter side
-  constexpr int RING = PK_B + NB * 64;
-  constexpr int PA_PER = kBM * 32 / kThreads;      // packed input-side entries per thread
-  constexpr int PB_PER = NB * 32 / kThreads;       // packed filter-side entries per thread
+  // The packed block's inputs land through direct-to-LDS element loads,
+  // which write each lane's element as a zero-extended 4-byte word:
+  // PK_B, its filter side (NB rows x 32 entries), and REM, the leftover
+  // channels of every slab position of every kd plane (taps * rp <= 32 and
+  // K_h K_w >= 4 bound K_d rp by 8: at most 8 planes of 18 x 34 entries).
+  constexpr int PK_B = F_BASE + 2 * B_BYTES;
+  constexpr int PB_PER = NB * 32 / kThreads;       // filter-side entries per thread
+  constexpr int REM = PK_B + NB * 32 * 4;
+  constexpr int REM_PER = (8 * (kRowsOut + 2) * kSW + kThreads - 1) / kThreads;   // REM entries per thread
+  constexpr int R_LOADS = REM_PER + PB_PER;        // element loads per thread
+  constexpr int RING = REM + REM_PER * kThreads * 4;
   constexpr int SEGB = 64 * NB + 16;               // one output row as laid out in y, plus the lead
-  constexpr int OUT = kRowsOut * SEGB;
+  constexpr int DUMMY = kRowsOut * SEGB;            // 64 dummy element slots
+  constexpr int OUT = DUMMY + 128;
   constexpr int SMEM = RING > OUT ? RING : OUT;
   static_assert(SMEM <= kLdsBytes, "LDS");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
@@ -185,7 +194,13 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
     b_pc[s] = ok ? c : (1 << 20);                  // past any cmain (< 2^23): never fetched
   }
 
-  u4 sreg[kALoads], freg[B_LOADS];
+  // The filter slice of step t goes out after the barrier that ends step
+  // t - 3, into register set t % KH, and is written to LDS before the barrier
+  // that ends step t - 1; the next slab's pieces go out during the steps
+  // before a slab's last and are written before its closing barrier.
+  // Every wave issues the same number of loads (its share, or out-of-range
+  // ones past the end), so the waits can count them.
+  u4 sreg[kALoads], freg[KH][B_LOADS];
   const int NG = sa.nch * p.kd;                    // slabs (chunk, kd), kd fastest
   // Past the last slab or step the loads fetch nothing (zeros, never written).
   int a_ic = 0, a_kd = 0;
@@ -205,20 +220,19 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
       a_ic += (int)wrap;
     }
   };
-  auto write_a = [&](int stage, int q0, int q1) __attribute__((always_inline)) {
+  auto write_a = [&](int stage) __attribute__((always_inline)) {
     char* sa_ = smem + stage * kSlabBytes;
 #pragma unroll
-    for (int q = q0; q < q1; ++q) *(u4*)(sa_ + (kWaves * q + wave) * 1024 + lane * 16) = sreg[q];
+    for (int q = 0; q < kALoads; ++q) *(u4*)(sa_ + (kWaves * q + wave) * 1024 + lane * 16) = sreg[q];
   };
   int b_ic = 0, b_kd = 0, b_kh = 0;                // next filter step: kh fastest
-  auto issue_b = [&]() __attribute__((always_inline)) {
+  auto issue_b = [&](u4(&fr)[B_LOADS]) __attribute__((always_inline)) {
     const int lim = sa.cmain - 32 * b_ic;
     const uint32_t woff = (uint32_t)((((b_kd * KH + b_kh) * KW) * p.cin + b_ic * 32) * 2);
 #pragma unroll
     for (int s = 0; s < B_LOADS; ++s)
-      if ((s + 1 < B_LOADS || B_PIECES % kThreads == 0) || s * kThreads + wave * 64 < B_PIECES)
-        freg[s] = __builtin_amdgcn_raw_buffer_load_b128(
-            wr, (b_base[s] + woff) | ((uint32_t)(8 * b_pc[s] + 8 > lim) << 31), 0, 0);
+      fr[s] = __builtin_amdgcn_raw_buffer_load_b128(wr, (b_base[s] + woff) | ((uint32_t)(8 * b_pc[s] + 8 > lim) << 31),
+                                                    0, 0);
     const int h1 = b_kh + 1;
     const bool wh = h1 == KH;
     b_kh = wh ? 0 : h1;
@@ -227,12 +241,12 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
     b_kd = wd ? 0 : d1;
     b_ic += (int)wd;
   };
-  auto write_b = [&](int stage) __attribute__((always_inline)) {
+  auto write_b = [&](const u4(&fr)[B_LOADS], int stage) __attribute__((always_inline)) {
     char* sb = smem + F_BASE + stage * B_BYTES;
 #pragma unroll
     for (int s = 0; s < B_LOADS; ++s)
       if ((s + 1 < B_LOADS || B_PIECES % kThreads == 0) || s * kThreads + wave * 64 < B_PIECES)
-        *(u4*)(sb + (s * kThreads + tid) * 16) = freg[s];
+        *(u4*)(sb + (s * kThreads + tid) * 16) = fr[s];
   };
 
   // ---- fragment addresses: lane (rr = lane % 16, g = lane / 16) reads piece g
@@ -256,78 +270,95 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
       for (int b = 0; b < NF; ++b) acc[a][b] = mfma16x16x32(bf[b], af[a], acc[a][b]);
   };
 
-  // ---- prologue: the loads of slab 0 and of the filter of step 0 go out,
-  // then the packed block is gathered element by element into its own LDS
-  // area (the input side as 512 rows x 32 entries laid out and swizzled like
-  // slab positions, the filter side as NB rows x 32 entries); its MFMAs run
-  // after the K loop, so that no accumulator is live while the gathers are.
-  // Thread t gathers entry t % 32 of rows t / 32 + 8 i: its tap and channel
-  // are fixed. ----
+  // ---- prologue: slab 0 and the filter slices of steps 0 to 2 (the first
+  // two land before the first barrier).  The packed block's element loads
+  // (REM position (kd, r, o), channel cmain + c at entry ((kd 18 + r) 34 +
+  // o) rp + c; PK_B entry e of filter row n at 32 n + e) go out during the
+  // last slab, whose steps fetch no slab pieces. ----
+  const bool packed = sa.npe > 0;
   if (NG > 0) {
     issue_a(0, kALoads);
-    issue_b();
+    issue_b(freg[0]);
+    issue_b(freg[1 % KH]);
   }
-  const bool packed = sa.npe > 0;
-  if (packed) {
-    const int el = tid & 31, r0 = tid >> 5;
-    const int tt = min(fast_div(el, sa.rp, sa.m_rp), p.ntaps - 1);   // entries past npe: any tap
-    const int c = sa.cmain + el - tt * sa.rp;
-    const int kw = tt % KW, t1 = tt / KW;
-    const int kh = t1 % KH, kd = t1 / KH;
-    const bool live = el < sa.npe;
-    const uint32_t toff = (uint32_t)((kd * p.ed * p.xs_d + kh * p.xs_h + kw * p.xs_w + c) * 2);
-    const bool dok = live && ((dmask >> kd) & 1u) != 0u;
-    uint32_t hv[PA_PER], hw[PB_PER];
+  // Element load i of the packed block's inputs (i < REM_PER: REM round i,
+  // else PK_B round i - REM_PER); out of range (nothing) when not packed, so
+  // that every wave issues the same count.
+  const int nrem = packed ? p.kd * (kRowsOut + 2) * kSW * sa.rp : 0;
+  auto issue_r = [&](int i0, int i1) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < PA_PER; ++i) {
-      const int row = r0 + 8 * i, th = row >> 5, pos = row & 31;
-      const bool ok = dok && (unsigned)(y0 + th + kh) < (unsigned)p.h && (unsigned)(x0 + pos + kw) < (unsigned)p.w;
-      const uint32_t off = ubase + __umul24((unsigned)th, rowB) + __umul24((unsigned)pos, posB) + toff;
-      hv[i] = __builtin_amdgcn_raw_buffer_load_b16(xr, off | ((uint32_t)!ok << 31), 0, 0);
+    for (int i = i0; i < i1; ++i) {
+      if (i < REM_PER) {
+        const int idx = i * kThreads + tid;
+        const int q = fast_div(idx, sa.rp, sa.m_rp), c = idx - q * sa.rp;
+        const int kd = q / ((kRowsOut + 2) * kSW), pos = q - kd * ((kRowsOut + 2) * kSW);
+        const int r = pos / kSW, o = pos - r * kSW;
+        const bool ok = idx < nrem && ((dmask >> min(kd, 31)) & 1u) != 0u && r < kRowsOut + KH - 1 &&
+                        o < kSeg + KW - 1 && (unsigned)(y0 + r) < (unsigned)p.h && (unsigned)(x0 + o) < (unsigned)p.w;
+        const uint32_t off = ubase + (uint32_t)((kd * p.ed * p.xs_d + sa.cmain + c) * 2) +
+                             __umul24((unsigned)r, rowB) + __umul24((unsigned)o, posB);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(smem + REM + (i * kThreads + wave * 64) * 4), 2,
+                                                 off | ((uint32_t)!ok << 31), 0, 0, 0);
+      } else {
+        const int ib = i - REM_PER;
+        const int el = tid & 31, n = n0 + (tid >> 5) + 8 * ib;
+        const int tt = min(fast_div(el, sa.rp, sa.m_rp), p.ntaps - 1);   // entries past npe: any tap
+        const uint32_t woffe = (uint32_t)((tt * p.cin + sa.cmain + el - tt * sa.rp) * 2);
+        const bool ok = packed && el < sa.npe && n < p.cout;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(smem + PK_B + (ib * kThreads + wave * 64) * 4), 2,
+                                                 (__umul24((unsigned)n, K2) + woffe) | ((uint32_t)!ok << 31), 0, 0, 0);
+      }
     }
-    const uint32_t woffe = (uint32_t)((tt * p.cin + c) * 2);
-#pragma unroll
-    for (int i = 0; i < PB_PER; ++i) {
-      const int n = n0 + r0 + 8 * i;
-      const bool ok = live && n < p.cout;
-      hw[i] = __builtin_amdgcn_raw_buffer_load_b16(wr, (__umul24((unsigned)n, K2) + woffe) | ((uint32_t)!ok << 31),
-                                                   0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < PA_PER; ++i) {
-      const int row = r0 + 8 * i;
-      *(uint16_t*)(smem + PK_A + row * 64 + swz(row, el >> 3) * 16 + (el & 7) * 2) = (uint16_t)hv[i];
-    }
-#pragma unroll
-    for (int i = 0; i < PB_PER; ++i) {
-      const int row = r0 + 8 * i;
-      *(uint16_t*)(smem + PK_B + row * 64 + swz(row, el >> 3) * 16 + (el & 7) * 2) = (uint16_t)hw[i];
-    }
-    if (NG == 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  if (NG > 0) {
+    wait_vmcnt<B_LOADS>();                         // all but the filter of step 1
+    write_a(0);
+    write_b(freg[0], 0);
+    issue_b(freg[2 % KH]);                         // (its set is free once step 0's is written)
+  } else {
+    issue_r(0, R_LOADS);                           // no K loop: the packed block's loads now
   }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   if (NG > 0) {
-    wait_vmcnt<0>();
-    write_a(0, 0, kALoads);
-    write_b(0);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    issue_b();                                     // filter of step 1
-    // block kw of every step computes on fragment set kw and reads the next
-    // block's set meanwhile (the last block: the next step's set 0)
-    V8 fa[KW][kFA], fb[KW][NF];
-    auto read_block = [&](V8(&af)[kFA], V8(&bf)[NF], const char* sa_, const char* sb, int kw)
-        __attribute__((always_inline)) {
-#pragma unroll
-      for (int a = 0; a < kFA; ++a) af[a] = *(const V8*)(sa_ + a_addr[kw] + ((a >> 1) * kSW + 16 * (a & 1)) * 64);
+    // A block multiplies the fragments fa (input, one set, refilled with the
+    // next block's fragment a right after fragment a's MFMAs are issued) and
+    // fb[kw] (filter: block kw of every step uses set kw and reads the next
+    // block's set, the last block the next step's set 0, before its MFMAs).
+    V8 fa[kFA], fb[KW][NF];
+    auto read_a = [&](const char* sa_, int kw, int a) __attribute__((always_inline)) {
+      return *(const V8*)(sa_ + a_addr[kw] + ((a >> 1) * kSW + 16 * (a & 1)) * 64);
+    };
+    auto read_b = [&](V8(&bf)[NF], const char* sb, int kw) __attribute__((always_inline)) {
 #pragma unroll
       for (int b = 0; b < NF; ++b) bf[b] = *(const V8*)(sb + b_addr + (kw * NB + 16 * b) * 64);
     };
-    read_block(fa[0], fb[0], smem, smem + F_BASE, 0);
+    // the MFMAs of a block on (fa, bf), fa refilled from (na, nkw); the next
+    // block's fragment reads go out one after every third MFMA (left to
+    // itself the scheduler issues them in one burst at the block's end, and
+    // with one wave per SIMD the matrix unit then waits for LDS)
+    auto mma_stream = [&](const V8(&bf)[NF], const char* na, int nkw) __attribute__((always_inline)) {
+#pragma unroll
+      for (int a = 0; a < kFA; ++a) {
+#pragma unroll
+        for (int b = 0; b < NF; ++b) acc[a][b] = mfma16x16x32(bf[b], fa[a], acc[a][b]);
+        fa[a] = read_a(na, nkw, a);
+      }
+#pragma unroll
+      for (int i = 0; i < kFA * NF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i % 3 == 2 && i / 3 < kFA + NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+#pragma unroll
+    for (int a = 0; a < kFA; ++a) fa[a] = read_a(smem, 0, a);
+    read_b(fb[0], smem + F_BASE, 0);
     int fs = 0;                                    // filter stage of the step being computed
-    // Step kh of slab g: K_w blocks.  The step fetches its share of the next
-    // slab's pieces (in the shadow of its first blocks) and the filter of the
-    // next step; its last block writes both to LDS, passes the barrier and
-    // reads the next step's first fragments before its MFMAs.
+    // Step kh of slab g: K_w blocks.  In the shadow of its first blocks the
+    // step fetches its share of the next slab's pieces; its last block waits
+    // for the next step's filter (closing a slab: and the next slab), writes
+    // them to LDS, passes the barrier, reads the next step's first fragments
+    // and fetches the filter three steps on before its MFMAs.
     auto plane = [&](int gi, auto final_c) __attribute__((always_inline)) {
       constexpr bool kFinal = decltype(final_c)::value;
       const char* sa0 = smem + (gi & 1) * kSlabBytes;
@@ -335,7 +366,16 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
       static_for<0, KH>([&](auto khc) __attribute__((always_inline)) {
         constexpr int kh = decltype(khc)::value;
         constexpr bool kLastStep = kFinal && kh + 1 == KH;
-        constexpr int q0 = kh * kALoads / KH, q1 = (kh + 1) * kALoads / KH;   // this step's slab pieces
+        // slab pieces of this step: [q0, q1) (none in a slab's last step)
+        constexpr int q0 = kh * kALoads / (KH - 1), q1 = kh + 1 < KH ? (kh + 1) * kALoads / (KH - 1) : q0;
+        constexpr int qprev = kh == 0 ? 0 : q0 - (kh - 1) * kALoads / (KH - 1);   // issued in the step before
+        // the last slab's steps issue the packed block's element loads instead
+        constexpr int r0 = kh * R_LOADS / (KH - 1), r1 = kh + 1 < KH ? (kh + 1) * R_LOADS / (KH - 1) : r0;
+        constexpr int rprev = kh == 0 ? 0 : r0 - (kh - 1) * R_LOADS / (KH - 1);
+        // loads newer than the next step's filter: the pieces of the step
+        // before, the filter two steps on, this step's pieces; closing a slab
+        // only that filter (the pieces all went out before it)
+        constexpr int kNewer = kh + 1 == KH ? B_LOADS : (kFinal ? rprev + (r1 - r0) : qprev + (q1 - q0)) + B_LOADS;
         const char* sak = sa0 + kh * kSW * 64;
         const char* sb = smem + F_BASE + fs * B_BYTES;
         const char* nak = kh + 1 < KH ? sa0 + (kh + 1) * kSW * 64 : sn;
@@ -344,21 +384,22 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
           constexpr int j = decltype(jc)::value;
           constexpr int cur = j, nxt = j + 1 < KW ? j + 1 : 0;
           if constexpr (j + 1 < KW) {
-            read_block(fa[nxt], fb[nxt], sak, sb, j + 1);
-            if constexpr (!kLastStep) issue_a(q0 + j * (q1 - q0) / (KW - 1), q0 + (j + 1) * (q1 - q0) / (KW - 1));
-            mma_block(fa[cur], fb[cur]);
+            read_b(fb[nxt], sb, j + 1);
+            if constexpr (!kFinal && q1 > q0) issue_a(q0 + j * (q1 - q0) / (KW - 1), q0 + (j + 1) * (q1 - q0) / (KW - 1));
+            if constexpr (kFinal && r1 > r0) issue_r(r0 + j * (r1 - r0) / (KW - 1), r0 + (j + 1) * (r1 - r0) / (KW - 1));
+            mma_stream(fb[cur], sak, j + 1);
             __builtin_amdgcn_sched_barrier(0);
           } else if constexpr (!kLastStep) {
-            wait_vmcnt<0>();
-            write_b(fs ^ 1);
-            write_a((gi + 1) & 1, q0, q1);
+            wait_vmcnt<kNewer>();
+            write_b(freg[(kh + 1) % KH], fs ^ 1);
+            if constexpr (kh + 1 == KH) write_a((gi + 1) & 1);
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            read_block(fa[nxt], fb[nxt], nak, nb, 0);
-            issue_b();                             // the step after next
-            mma_block(fa[cur], fb[cur]);
+            read_b(fb[nxt], nb, 0);
+            issue_b(freg[(kh + 3) % KH]);          // three steps on (the set just written, for K_h = 2)
+            mma_stream(fb[cur], nak, 0);
             __builtin_amdgcn_sched_barrier(0);
           } else {
-            mma_block(fa[cur], fb[cur]);
+            mma_block(fa, fb[cur]);
           }
         });
         fs ^= 1;
@@ -368,16 +409,45 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
     plane(NG - 1, std::true_type{});
   }
 
-  // ---- the packed block (its LDS area was written before the first barrier) ----
+  // ---- the packed block: its input-side fragments gathered from REM (lane
+  // entries e = 8 g + j: tap e / rp, channel e % rp), its filter side from
+  // PK_B; every wave's element loads have landed after the barrier ----
   if (packed) {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    int eoff[8];
+    uint32_t elive = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = 8 * g + j;
+      const int tt = min(fast_div(e, sa.rp, sa.m_rp), p.ntaps - 1);
+      const int c = e - tt * sa.rp;
+      const int kw = tt % KW, t1 = tt / KW;
+      const int kh = t1 % KH, kd = t1 / KH;
+      eoff[j] = (((kd * (kRowsOut + 2) + kh) * kSW + kw) * sa.rp + c) * 4;
+      elive |= (e < sa.npe ? 1u : 0u) << j;
+    }
     V8 pa[kFA], pw[NF];
 #pragma unroll
     for (int a = 0; a < kFA; ++a) {
-      const int row = (kRowsWave * wave + (a >> 1)) * 32 + 16 * (a & 1) + rr;
-      pa[a] = *(const V8*)(smem + PK_A + row * 64 + swz(row, g) * 16);
+      const int th = kRowsWave * wave + (a >> 1), pos = 16 * (a & 1) + rr;
+      const char* base = smem + REM + (th * kSW + pos) * sa.rp * 4;
+      u4 v;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = (elive >> (2 * d)) & 1u ? *(const uint32_t*)(base + eoff[2 * d]) : 0u;
+        const uint32_t hi = (elive >> (2 * d + 1)) & 1u ? *(const uint32_t*)(base + eoff[2 * d + 1]) : 0u;
+        v[d] = (lo & 0xffffu) | (hi << 16);
+      }
+      pa[a] = __builtin_bit_cast(V8, v);
     }
 #pragma unroll
-    for (int b = 0; b < NF; ++b) pw[b] = *(const V8*)(smem + PK_B + b_addr + 16 * b * 64);
+    for (int b = 0; b < NF; ++b) {
+      const char* row = smem + PK_B + (16 * b + rr) * 128 + g * 32;
+      const u4 e0 = *(const u4*)row, e1 = *(const u4*)(row + 16);
+      const u4 v = {(e0[0] & 0xffffu) | (e0[1] << 16), (e0[2] & 0xffffu) | (e0[3] << 16),
+                    (e1[0] & 0xffffu) | (e1[1] << 16), (e1[2] & 0xffffu) | (e1[3] << 16)};
+      pw[b] = __builtin_bit_cast(V8, v);
+    }
     mma_block(pa, pw);
   }
 
@@ -387,26 +457,34 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
     // Row th of the tile: outputs ow0 .. ow0 + nv - 1 of output row oh0 + th,
     // nv * C_out contiguous elements of y starting at byte address ga; in LDS
     // at seg + lead + the same byte offset, lead = ga % 16.
+    // Without branches: an element that is no output (past C_out, or past
+    // the output's end along w) goes to a dummy slot of its lane's own.
     const int nv = min(kSeg, p.ow - ow0);
+    const bool all_pos = nv == kSeg;
 #pragma unroll
     for (int hi = 0; hi < kRowsWave; ++hi) {
       const int th = kRowsWave * wave + hi;
       if (oh0 + th >= p.oh) continue;
       const int64_t m = ((int64_t)(img * p.od + od) * p.oh + oh0 + th) * p.ow + ow0;
       const int lead = (int)((uintptr_t)(y + m * p.cout) & 15);
-      char* seg = smem + th * SEGB + lead;
 #pragma unroll
       for (int ah = 0; ah < 2; ++ah) {
         const int a = 2 * hi + ah;
         const int pos = 16 * ah + rr;
-        if (pos < nv) {
+        const uint32_t pbase = (uint32_t)(th * SEGB + lead + 2 * pos * p.cout + 8 * g);
+        const bool pos_ok = pos < nv;
 #pragma unroll
-          for (int b = 0; b < NF; ++b)
+        for (int b = 0; b < NF; ++b) {
+          if (all_pos && 16 * b + 16 <= p.cout) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *(T*)(smem + pbase + 2 * (16 * b + i)) = from_f32<T>(acc[a][b][i]);
+          } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int n = 16 * b + 4 * g + i;
-              if (n < p.cout) *(T*)(seg + 2 * (pos * p.cout + n)) = from_f32<T>(acc[a][b][i]);
+              const bool ok = pos_ok && 16 * b + 4 * g + i < p.cout;
+              *(T*)(smem + (ok ? pbase + 2 * (16 * b + i) : (uint32_t)(DUMMY + 2 * lane))) = from_f32<T>(acc[a][b][i]);
             }
+          }
         }
       }
     }
