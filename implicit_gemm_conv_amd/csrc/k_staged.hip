@@ -75,6 +75,7 @@ constexpr int kALoads = 10;                         // 16-byte slab pieces per t
                                                     // 16 positions cover 18 x 34
 constexpr int kSlabBytes = kWaves * kALoads * 16 * 64;   // 40 KB a stage
 constexpr int kLdsBytes = 160 * 1024;
+constexpr int kMaxPackKd = 3;                       // depth taps with leftover channels
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
@@ -119,17 +120,18 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
   constexpr int B_PIECES = B_ROWS * 4;             // a multiple of 64
   constexpr int B_LOADS = (B_PIECES + kThreads - 1) / kThreads;
   constexpr int F_BASE = 2 * kSlabBytes;
-  // The packed block's inputs land through direct-to-LDS element loads,
-  // which write each lane's element as a zero-extended 4-byte word:
-  // PK_B, its filter side (NB rows x 32 entries), and REM, the leftover
-  // channels of every slab position of every kd plane (taps * rp <= 32 and
-  // K_h K_w >= 4 bound K_d rp by 8: at most 8 planes of 18 x 34 entries).
+  // The packed block's inputs land through direct-to-LDS loads: PK_B, its
+  // filter side (NB rows x 32 entries, 2-byte loads, each lane's element
+  // written as a zero-extended 4-byte word), and REM, per kd plane (at most
+  // 3) and slab position the 16 bytes that end the position, its last 8
+  // channels, the leftover ones among them (16-byte loads, a position a lane).
   constexpr int PK_B = F_BASE + 2 * B_BYTES;
   constexpr int PB_PER = NB * 32 / kThreads;       // filter-side entries per thread
   constexpr int REM = PK_B + NB * 32 * 4;
-  constexpr int REM_PER = (8 * (kRowsOut + 2) * kSW + kThreads - 1) / kThreads;   // REM entries per thread
-  constexpr int R_LOADS = REM_PER + PB_PER;        // element loads per thread
-  constexpr int RING = REM + REM_PER * kThreads * 4;
+  constexpr int REM_SLOTS = 3 * kThreads;          // slab positions (612 used) per kd plane
+  constexpr int REM_PER = REM_SLOTS / kThreads;    // REM loads per thread and plane
+  constexpr int R_LOADS = PB_PER;                  // filter-side element loads per thread
+  constexpr int RING = REM + kMaxPackKd * REM_SLOTS * 16;
   constexpr int SEGB = 64 * NB + 16;               // one output row as laid out in y, plus the lead
   constexpr int DUMMY = kRowsOut * SEGB;            // 64 dummy element slots
   constexpr int OUT = DUMMY + 128;
@@ -270,57 +272,57 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
       for (int b = 0; b < NF; ++b) acc[a][b] = mfma16x16x32(bf[b], af[a], acc[a][b]);
   };
 
-  // ---- prologue: slab 0 and the filter slices of steps 0 to 2 (the first
-  // two land before the first barrier).  The packed block's element loads
-  // (REM position (kd, r, o), channel cmain + c at entry ((kd 18 + r) 34 +
-  // o) rp + c; PK_B entry e of filter row n at 32 n + e) go out during the
-  // last slab, whose steps fetch no slab pieces. ----
+  // ---- prologue: slab 0 (with its REM plane), the filter slices of steps 0
+  // and 1, the packed block's filter-side loads (PK_B entry e of filter row n
+  // at 32 n + e) and the filter of step 2; slab 0 and the first filter land
+  // before the first barrier. ----
   const bool packed = sa.npe > 0;
-  if (NG > 0) {
-    issue_a(0, kALoads);
-    issue_b(freg[0]);
-    issue_b(freg[1 % KH]);
+  // REM loads of the slab about to be fetched (a_ic, a_kd): live in the last
+  // channel chunk (out of range otherwise, so that every slab issues them).
+  const uint32_t rtail = (uint32_t)(2 * p.cin - 16);
+  uint32_t r_base[REM_PER];
+#pragma unroll
+  for (int i = 0; i < REM_PER; ++i) {
+    const int pos = i * kThreads + tid, r = pos / kSW, o = pos - r * kSW;
+    const bool ok = packed && r < kRowsOut + KH - 1 && o < kSeg + KW - 1 && (unsigned)(y0 + r) < (unsigned)p.h &&
+                    (unsigned)(x0 + o) < (unsigned)p.w;
+    r_base[i] = ok ? ubase + __umul24((unsigned)r, rowB) + __umul24((unsigned)o, posB) + rtail : kOutOfRange;
   }
-  // Element load i of the packed block's inputs (i < REM_PER: REM round i,
-  // else PK_B round i - REM_PER); out of range (nothing) when not packed, so
-  // that every wave issues the same count.
-  const int nrem = packed ? p.kd * (kRowsOut + 2) * kSW * sa.rp : 0;
+  auto issue_rem = [&]() __attribute__((always_inline)) {
+    const bool live = a_ic == sa.nch - 1 && ((dmask >> a_kd) & 1u) != 0u;
+    const uint32_t zoff = (uint32_t)(a_kd * p.ed * p.xs_d * 2);
+#pragma unroll
+    for (int i = 0; i < REM_PER; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, (lds_ptr_t)(smem + REM + (min(a_kd, kMaxPackKd - 1) * REM_SLOTS + i * kThreads + wave * 64) * 16), 16,
+          live ? r_base[i] + zoff : kOutOfRange, 0, 0, 0);
+  };
+  issue_rem();
+  issue_a(0, kALoads);
+  issue_b(freg[0]);
+  issue_b(freg[1 % KH]);
+  // The packed block's filter-side load i, out of range when not packed.
   auto issue_r = [&](int i0, int i1) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
-      if (i < REM_PER) {
-        const int idx = i * kThreads + tid;
-        const int q = fast_div(idx, sa.rp, sa.m_rp), c = idx - q * sa.rp;
-        const int kd = q / ((kRowsOut + 2) * kSW), pos = q - kd * ((kRowsOut + 2) * kSW);
-        const int r = pos / kSW, o = pos - r * kSW;
-        const bool ok = idx < nrem && ((dmask >> min(kd, 31)) & 1u) != 0u && r < kRowsOut + KH - 1 &&
-                        o < kSeg + KW - 1 && (unsigned)(y0 + r) < (unsigned)p.h && (unsigned)(x0 + o) < (unsigned)p.w;
-        const uint32_t off = ubase + (uint32_t)((kd * p.ed * p.xs_d + sa.cmain + c) * 2) +
-                             __umul24((unsigned)r, rowB) + __umul24((unsigned)o, posB);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(smem + REM + (i * kThreads + wave * 64) * 4), 2,
-                                                 off | ((uint32_t)!ok << 31), 0, 0, 0);
-      } else {
-        const int ib = i - REM_PER;
-        const int el = tid & 31, n = n0 + (tid >> 5) + 8 * ib;
+      {
+        const int el = tid & 31, n = n0 + (tid >> 5) + 8 * i;
         const int tt = min(fast_div(el, sa.rp, sa.m_rp), p.ntaps - 1);   // entries past npe: any tap
         const uint32_t woffe = (uint32_t)((tt * p.cin + sa.cmain + el - tt * sa.rp) * 2);
         const bool ok = packed && el < sa.npe && n < p.cout;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(smem + PK_B + (ib * kThreads + wave * 64) * 4), 2,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(smem + PK_B + (i * kThreads + wave * 64) * 4), 2,
                                                  (__umul24((unsigned)n, K2) + woffe) | ((uint32_t)!ok << 31), 0, 0, 0);
       }
     }
   };
-  if (NG > 0) {
-    wait_vmcnt<B_LOADS>();                         // all but the filter of step 1
-    write_a(0);
-    write_b(freg[0], 0);
-    issue_b(freg[2 % KH]);                         // (its set is free once step 0's is written)
-  } else {
-    issue_r(0, R_LOADS);                           // no K loop: the packed block's loads now
-  }
+  issue_r(0, R_LOADS);
+  wait_vmcnt<B_LOADS + R_LOADS>();                 // all but the filter of step 1 and the filter-side loads
+  write_a(0);
+  write_b(freg[0], 0);
+  issue_b(freg[2 % KH]);                           // (its set is free once step 0's is written)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  if (NG > 0) {
+  {
     // A block multiplies the fragments fa (input, one set, refilled with the
     // next block's fragment a right after fragment a's MFMAs are issued) and
     // fb[kw] (filter: block kw of every step uses set kw and reads the next
@@ -353,6 +355,48 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
 #pragma unroll
     for (int a = 0; a < kFA; ++a) fa[a] = read_a(smem, 0, a);
     read_b(fb[0], smem + F_BASE, 0);
+    // The packed block: its input-side fragments gathered from REM (lane
+    // entries e = 8 g + j: tap e / rp, channel cmain + e % rp, element 8 - rp
+    // + e % rp of the position's last 16 bytes), its filter side from PK_B.
+    // Both are in LDS from the last slab on (its REM plane was fetched during
+    // the slab before, PK_B in the prologue); the gathers go out in its first
+    // step, the MFMAs follow its last block's.
+    V8 pa[kFA], pw[NF];
+    auto gather_pack = [&]() __attribute__((always_inline)) {
+      int eoff[8];
+      uint32_t elive = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = 8 * g + j;
+        const int tt = min(fast_div(e, sa.rp, sa.m_rp), p.ntaps - 1);
+        const int c = e - tt * sa.rp;
+        const int kw = tt % KW, t1 = tt / KW;
+        const int kh = t1 % KH, kd = t1 / KH;
+        eoff[j] = ((kd * REM_SLOTS + kh * kSW + kw) * 16) + (8 - sa.rp + c) * 2;
+        elive |= (e < sa.npe ? 1u : 0u) << j;
+      }
+#pragma unroll
+      for (int a = 0; a < kFA; ++a) {
+        const int th = kRowsWave * wave + (a >> 1), pos = 16 * (a & 1) + rr;
+        const char* base = smem + REM + (th * kSW + pos) * 16;
+        u4 v;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t lo = (elive >> (2 * d)) & 1u ? *(const uint16_t*)(base + eoff[2 * d]) : 0u;
+          const uint32_t hi = (elive >> (2 * d + 1)) & 1u ? *(const uint16_t*)(base + eoff[2 * d + 1]) : 0u;
+          v[d] = lo | (hi << 16);
+        }
+        pa[a] = __builtin_bit_cast(V8, v);
+      }
+#pragma unroll
+      for (int b = 0; b < NF; ++b) {
+        const char* row = smem + PK_B + (16 * b + rr) * 128 + g * 32;
+        const u4 e0 = *(const u4*)row, e1 = *(const u4*)(row + 16);
+        const u4 v = {(e0[0] & 0xffffu) | (e0[1] << 16), (e0[2] & 0xffffu) | (e0[3] << 16),
+                      (e1[0] & 0xffffu) | (e1[1] << 16), (e1[2] & 0xffffu) | (e1[3] << 16)};
+        pw[b] = __builtin_bit_cast(V8, v);
+      }
+    };
     int fs = 0;                                    // filter stage of the step being computed
     // Step kh of slab g: K_w blocks.  In the shadow of its first blocks the
     // step fetches its share of the next slab's pieces; its last block waits
@@ -368,14 +412,14 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
         constexpr bool kLastStep = kFinal && kh + 1 == KH;
         // slab pieces of this step: [q0, q1) (none in a slab's last step)
         constexpr int q0 = kh * kALoads / (KH - 1), q1 = kh + 1 < KH ? (kh + 1) * kALoads / (KH - 1) : q0;
-        constexpr int qprev = kh == 0 ? 0 : q0 - (kh - 1) * kALoads / (KH - 1);   // issued in the step before
-        // the last slab's steps issue the packed block's element loads instead
-        constexpr int r0 = kh * R_LOADS / (KH - 1), r1 = kh + 1 < KH ? (kh + 1) * R_LOADS / (KH - 1) : r0;
-        constexpr int rprev = kh == 0 ? 0 : r0 - (kh - 1) * R_LOADS / (KH - 1);
+        // loads the step issues ahead of the next slab: its pieces, and in the
+        // first step the next slab's REM plane
+        constexpr int nq = q1 - q0 + (kh == 0 ? REM_PER : 0);
+        constexpr int qprev = kh == 0 ? 0 : q0 - (kh - 1) * kALoads / (KH - 1) + (kh == 1 ? REM_PER : 0);
         // loads newer than the next step's filter: the pieces of the step
         // before, the filter two steps on, this step's pieces; closing a slab
         // only that filter (the pieces all went out before it)
-        constexpr int kNewer = kh + 1 == KH ? B_LOADS : (kFinal ? rprev + (r1 - r0) : qprev + (q1 - q0)) + B_LOADS;
+        constexpr int kNewer = kh + 1 == KH ? B_LOADS : (kFinal ? 0 : qprev + nq) + B_LOADS;
         const char* sak = sa0 + kh * kSW * 64;
         const char* sb = smem + F_BASE + fs * B_BYTES;
         const char* nak = kh + 1 < KH ? sa0 + (kh + 1) * kSW * 64 : sn;
@@ -385,8 +429,11 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
           constexpr int cur = j, nxt = j + 1 < KW ? j + 1 : 0;
           if constexpr (j + 1 < KW) {
             read_b(fb[nxt], sb, j + 1);
+            if constexpr (!kFinal && kh == 0 && j == 0) issue_rem();
+            if constexpr (kFinal && kh == 0 && j == 0) {
+              if (packed) gather_pack();
+            }
             if constexpr (!kFinal && q1 > q0) issue_a(q0 + j * (q1 - q0) / (KW - 1), q0 + (j + 1) * (q1 - q0) / (KW - 1));
-            if constexpr (kFinal && r1 > r0) issue_r(r0 + j * (r1 - r0) / (KW - 1), r0 + (j + 1) * (r1 - r0) / (KW - 1));
             mma_stream(fb[cur], sak, j + 1);
             __builtin_amdgcn_sched_barrier(0);
           } else if constexpr (!kLastStep) {
@@ -400,6 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
             __builtin_amdgcn_sched_barrier(0);
           } else {
             mma_block(fa, fb[cur]);
+            if (packed) mma_block(pa, pw);
           }
         });
         fs ^= 1;
@@ -407,48 +455,6 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
     };
     for (int gi = 0; gi + 1 < NG; ++gi) plane(gi, std::false_type{});
     plane(NG - 1, std::true_type{});
-  }
-
-  // ---- the packed block: its input-side fragments gathered from REM (lane
-  // entries e = 8 g + j: tap e / rp, channel e % rp), its filter side from
-  // PK_B; every wave's element loads have landed after the barrier ----
-  if (packed) {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    int eoff[8];
-    uint32_t elive = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = 8 * g + j;
-      const int tt = min(fast_div(e, sa.rp, sa.m_rp), p.ntaps - 1);
-      const int c = e - tt * sa.rp;
-      const int kw = tt % KW, t1 = tt / KW;
-      const int kh = t1 % KH, kd = t1 / KH;
-      eoff[j] = (((kd * (kRowsOut + 2) + kh) * kSW + kw) * sa.rp + c) * 4;
-      elive |= (e < sa.npe ? 1u : 0u) << j;
-    }
-    V8 pa[kFA], pw[NF];
-#pragma unroll
-    for (int a = 0; a < kFA; ++a) {
-      const int th = kRowsWave * wave + (a >> 1), pos = 16 * (a & 1) + rr;
-      const char* base = smem + REM + (th * kSW + pos) * sa.rp * 4;
-      u4 v;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = (elive >> (2 * d)) & 1u ? *(const uint32_t*)(base + eoff[2 * d]) : 0u;
-        const uint32_t hi = (elive >> (2 * d + 1)) & 1u ? *(const uint32_t*)(base + eoff[2 * d + 1]) : 0u;
-        v[d] = (lo & 0xffffu) | (hi << 16);
-      }
-      pa[a] = __builtin_bit_cast(V8, v);
-    }
-#pragma unroll
-    for (int b = 0; b < NF; ++b) {
-      const char* row = smem + PK_B + (16 * b + rr) * 128 + g * 32;
-      const u4 e0 = *(const u4*)row, e1 = *(const u4*)(row + 16);
-      const u4 v = {(e0[0] & 0xffffu) | (e0[1] << 16), (e0[2] & 0xffffu) | (e0[3] << 16),
-                    (e1[0] & 0xffffu) | (e1[1] << 16), (e1[2] & 0xffffu) | (e1[3] << 16)};
-      pw[b] = __builtin_bit_cast(V8, v);
-    }
-    mma_block(pa, pw);
   }
 
   // ---- epilogue ----
@@ -583,7 +589,7 @@ bool staged_accepts(const ConvParams& p, int dtype) {
                         ((p.cout + 31) / 32);
   return (dtype == kF16 || dtype == kBF16) && p.remap == 0 && p.groups == 1 && p.sh == 1 && p.sw == 1 &&
          p.eh == 1 && p.ew == 1 && p.kh >= 2 && p.kh <= 3 && p.kw >= 2 && p.kw <= 3 && p.kd <= 16 &&
-         (int64_t)p.ntaps * (p.cin % 8) <= 32 &&
+         p.cin >= 8 && (int64_t)p.ntaps * (p.cin % 8) <= 32 && (p.cin % 8 == 0 || p.kd <= kMaxPackKd) &&
          // 32-bit buffer offsets, the set-up's 24-bit multiplies and tile decode
          (int64_t)p.n * p.xs_n * 2 < ((int64_t)1 << 31) && (int64_t)p.cout * p.K * 2 < ((int64_t)1 << 31) &&
          (int64_t)p.xs_h * 2 < (1 << 24) && (int64_t)p.K * 2 < (1 << 24) && tiles < (1 << 24);

@@ -59,7 +59,7 @@ CANARY = [
     ("grouped", "bf16", (2, 9, 10, 12), (18, 3, 3, 2), (1, 1), (1, 1), 6),
     ("staged", "bf16", (1, 3, 19, 37, 65), (65, 3, 3, 3, 65), (1, 1, 1), (1, 1, 1), 1),
     ("staged", "fp16", (2, 18, 40, 33), (130, 3, 2, 33), (1, 1), (1, 1), 1),
-    ("staged", "fp16", (1, 4, 16, 32, 1), (24, 3, 3, 3, 1), (1, 1, 1), (1, 1, 1), 1),
+    ("staged", "fp16", (1, 4, 16, 32, 9), (24, 3, 3, 3, 9), (1, 1, 1), (1, 1, 1), 1),
 ]
 
 

@@ -74,8 +74,8 @@ CASES = [
     # blocks, 80-, 64- and 32-channel tiles, two column tiles (element-wise stores), pack only
     _case("staged_bf16_c65_o65_ragged", "bf16", (1, 5, 19, 37, 65), (65, 3, 3, 3, 65), (1, 1, 1), (1, 1, 1),
           seed=36),
-    _case("staged_fp16_c1_pack_only", "fp16", (2, 6, 20, 33, 1), (24, 3, 3, 3, 1), (1, 1, 1), (1, 1, 1), seed=37),
-    _case("staged_bf16_2d_c3_o40", "bf16", (3, 21, 40, 3), (40, 3, 3, 3), (1, 1), (1, 1), seed=38),
+    _case("staged_fp16_c9_one_piece", "fp16", (2, 6, 20, 33, 9), (24, 3, 3, 3, 9), (1, 1, 1), (1, 1, 1), seed=37),
+    _case("staged_bf16_2d_c11_o40", "bf16", (3, 21, 40, 11), (40, 3, 3, 11), (1, 1), (1, 1), seed=38),
     _case("staged_fp16_c40_partial_chunk", "fp16", (1, 4, 18, 34, 40), (33, 3, 3, 3, 40), (1, 1, 1), (1, 1, 1),
           seed=39),
     _case("staged_fp16_2d_c33_o130_kw2", "fp16", (2, 18, 35, 33), (130, 3, 2, 33), (1, 1), (1, 0), seed=40),
@@ -103,8 +103,11 @@ def _accepts(wl, path):
         return (half and wl.x_shape[-1] % 64 == 0 and wl.stride[-1] == 2 and wl.stride[-2] == 2
                 and wl.w_shape[-2] in (2, 3) and wl.w_shape[-3] in (2, 3))
     if path == "staged":
+        cin = wl.x_shape[-1]
+        kd = wl.w_shape[1] if len(wl.w_shape) == 5 else 1
         return (wl.dtype in ("fp16", "bf16") and wl.stride[-1] == 1 and wl.stride[-2] == 1
-                and wl.w_shape[-2] in (2, 3) and wl.w_shape[-3] in (2, 3) and (wl.x_shape[-1] % 8) * taps <= 32)
+                and wl.w_shape[-2] in (2, 3) and wl.w_shape[-3] in (2, 3) and cin >= 8
+                and (cin % 8) * taps <= 32 and (cin % 8 == 0 or kd <= 3))
     if path == "brick":
         return half and wl.x_shape[-1] % 16 == 0 and taps >= 4
     if path == "rows":
@@ -217,7 +220,7 @@ EXACT = [
     ("phase", "fp16", (1, 4, 20, 21, 64), (2, 2, 2), (1, 2, 2), (0, 1, 0)),
     ("staged", "bf16", (1, 4, 17, 35, 65), (3, 3, 3), (1, 1, 1), (1, 1, 1)),
     ("staged", "fp16", (2, 3, 16, 33, 17), (3, 2, 3), (2, 1, 1), (1, 0, 2)),
-    ("staged", "fp16", (1, 2, 18, 32, 2), (2, 3, 2), (1, 1, 1), (1, 1, 0)),
+    ("staged", "fp16", (1, 2, 18, 32, 10), (2, 3, 2), (1, 1, 1), (1, 1, 0)),
     ("staged", "bf16", (2, 17, 40, 40), (3, 3), (1, 1), (1, 1)),
 ]
 
@@ -406,8 +409,10 @@ def _v_accepts(v, path):
                 and cin_g % 64 == 0 and ws[0] % 4 == 0 and st[-1] == 2 and st[-2] == 2
                 and ws[-2] in (2, 3) and ws[-3] in (2, 3))
     if path == "staged":
+        kd = ws[1] if len(ws) == 5 else 1
         return (half and g == 1 and dil[-1] == 1 and dil[-2] == 1 and st[-1] == 1 and st[-2] == 1
-                and ws[-2] in (2, 3) and ws[-3] in (2, 3) and (xs[-1] % 8) * int(np.prod(ws[1:-1])) <= 32)
+                and ws[-2] in (2, 3) and ws[-3] in (2, 3) and xs[-1] >= 8
+                and (xs[-1] % 8) * int(np.prod(ws[1:-1])) <= 32 and (xs[-1] % 8 == 0 or kd <= 3))
     if path == "slab":
         return (half and (g == 1 or cout_g % 64 == 0) and dil[-1] == dil[-2]
                 and (dil[-1] == 1 or (dil[-1] == 2 and ws[-2] == 3 and ws[-3] == 3))
