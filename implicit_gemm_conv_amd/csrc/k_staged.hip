@@ -1,7 +1,8 @@
 // k_staged.hip -- the slab scheme for channel counts that are not a multiple
 // of 32, and for tensors that are aligned to their element size only
 // (fp16/bf16, one group, unit stride and no dilation along h and w, K_h and
-// K_w in {2, 3}; any C_in with (C_in mod 8) * K_d * K_h * K_w <= 32).
+// K_w in {2, 3}; C_in >= 8 with (C_in mod 8) * K_d * K_h * K_w <= 32, and
+// K_d <= 3 when C_in mod 8 != 0).
 //
 // The classic implicit GEMM ("Convolutions" tutorial, section 5) gathers each
 // tap's A tile afresh, although neighbouring taps read the same input moved
@@ -19,7 +20,11 @@
 //    slab walk, one K block of 32 per (chunk, tap);
 //  * the r = C_in mod 8 channels left over, over all T = K_d K_h K_w taps:
 //    T r <= 32 entries (tap-major, channel-minor, the filter's own order)
-//    packed into one more K block, gathered element by element once per tile.
+//    packed into one more K block.  Its input side comes from the 16 bytes
+//    that end every slab position (fetched with the slab of each depth tap
+//    of the last chunk), gathered element by element into fragments during
+//    the last slab; its filter side is fetched element by element at the
+//    start.
 // On (4, 32^3, 65 -> 65) the depth is 2 x 27 chunk blocks + 1 packed block
 // (1760 columns for 1755) where 32-channel padding would take 81 blocks.
 //
@@ -35,11 +40,13 @@
 // double-buffered fragments and the loads in flight.)
 //
 // Pipeline, per K step (chunk, kd, kh) of K_w blocks: the filter slice of
-// step s + 1 is fetched into registers after the barrier that starts step s
-// and written to its LDS stage before the barrier that ends it; the slab of
-// the next (chunk, kd) is fetched during the first step of the current one
-// and written before its last step's closing barrier.  Fragments of the next
-// block are read while the current block's MFMAs run.  LDS: slab position o
+// step t is fetched into registers (one of K_h sets) after the barrier that
+// ends step t - 3 and written to its LDS stage before the barrier that ends
+// step t - 1; the pieces of the next (chunk, kd) slab are fetched during the
+// steps before a slab's last and written before its closing barrier.  With
+// one wave per SIMD nothing else hides latency, so the next block's fragment
+// reads are interleaved one after every third MFMA of the current block (the
+// scheduler would otherwise issue them in one burst).  LDS: slab position o
 // of row r at (34 r + o) * 64 bytes, filter row kw NB + n at (kw NB + n) * 64,
 // their four 16-byte pieces XOR-swizzled by bits 2..3 of o (of the row), so
 // that 16 lanes reading 16 consecutive positions hit distinct bank groups.

@@ -118,8 +118,9 @@ typedef enum {
                               windows cover are staged in LDS split by stride phase (even rows and
                               odd rows, each row's even positions before its odd ones), so every
                               tap reads consecutive slots, MFMA */
-  CONVFWD_PATH_STAGED = 11 /* fp16/bf16, G = 1, any C_in with (C_in % 8) * K_d*K_h*K_w <= 32, stride 1
-                              and dilation 1 along h and w, K_h and K_w in {2, 3}, K_d <= 16,
+  CONVFWD_PATH_STAGED = 11 /* fp16/bf16, G = 1, C_in >= 8 with (C_in % 8) * K_d*K_h*K_w <= 32 (and K_d <= 3
+                              when C_in % 8 != 0), stride 1 and dilation 1 along h and w, K_h and
+                              K_w in {2, 3}, K_d <= 16,
                               element-aligned tensors suffice: the slab scheme with the input
                               staged through registers (unaligned 16-byte loads, so positions of
                               any channel count), tiles of 16 output rows x 32 outputs x 32, 64
