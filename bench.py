@@ -14,9 +14,12 @@ The JSON line also carries
                 launch stream (one before each launch, each launch timed to
                 the next event; timing-only events, recorded without a
                 system-scope fence), against the MI355X dense fp16 MFMA peak;
-  cpu_baseline: the float64 CPU oracle on a bounded sample of the same
-                workload (a fixed set of output rows of the first convolution),
-                on this host's cores, rank 0 only.
+                The same object carries the kernel-trace figure of the committed
+                rocprofv3 summary (trace_us, trace_frac) when that summary was
+                taken on the current kernel sources;
+  cpu_baseline: the float64 CPU oracle (OpenMP over this host's cores) on a
+                share of one step's output rows (--cpu-fraction, default the
+                whole step: every output row of the three convolutions).
 
 ``--sweep`` instead times every workload shape on its own (10 warm-ups, then
 ``--launches`` launches each between two HIP events on the launch stream;
@@ -137,6 +140,25 @@ def stored_traffic(path):
     if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash(path):
         return None
     return float(m_bytes.group(1))
+
+
+def trace_file(path):
+    return os.path.join(ROOT, "profiles", "conv_fp16_c4_sweep_kernel_trace.md")
+
+
+def stored_trace_ns(path):
+    """Mean kernel-trace duration per launch of the path's kernel from the committed rocprofv3
+    summary of this bench, or None when missing or taken on other kernel sources."""
+    f = trace_file(path)
+    if path not in KERNELS or not os.path.exists(f):
+        return None
+    text = open(f).read()
+    m_path = re.search(r"dominant_path:\s*(\w+)", text)
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_ns = re.search(r"dominant_kernel_trace_mean_ns:\s*([0-9.]+)", text)
+    if not (m_path and m_hash and m_ns) or m_path.group(1) != path or m_hash.group(1) != kernel_source_hash(path):
+        return None
+    return float(m_ns.group(1))
 
 
 def copy_calibration(mib=512, reps=5):
@@ -357,12 +379,18 @@ def main():
                  for wl in wls]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp16"],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp16"], 4),
+                "timer": "HIP events on the launch stream, one per launch, each launch timed to the next event",
                 "traffic": stored_traffic(dom_path),
                 "kernel": KERNELS.get(dom_path, (dom_path,))[0] + " (" +
                           ", ".join(wls[i].name.split("_")[0] for i in dom) + ")",
                 "kernel_source_sha256": kernel_source_hash(dom_path) if dom_path in KERNELS else None,
                 "launch_us": round(dom_us, 3), "flops_per_launch": dom_flops,
                 "algorithmic_bytes_per_launch": float(np.mean([alg_bytes[i] for i in dom]))}
+    trace_ns = stored_trace_ns(dom_path)
+    if trace_ns is not None:
+        roofline["trace_us"] = round(trace_ns / 1e3, 3)
+        roofline["trace_frac"] = round(dom_flops / (trace_ns * 1e-9) / 1e12 / PEAK_TFLOPS["fp16"], 4)
+        roofline["trace_profile"] = os.path.relpath(trace_file(dom_path), ROOT)
 
     value = step_flops * args.steps / (total_ms * 1e-3) / 1e12
     rec = {

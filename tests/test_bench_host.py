@@ -44,3 +44,22 @@ def test_every_listed_kernel_source_exists():
     for path, (_, files) in bench.KERNELS.items():
         for rel in files:
             assert os.path.exists(os.path.join(bench.ROOT, rel)), (path, rel)
+
+
+def test_stored_trace_needs_the_path_and_the_matching_hash(fake_kernel, tmp_path, monkeypatch):
+    summary = tmp_path / "trace.md"
+    monkeypatch.setattr(bench, "trace_file", lambda path: str(summary))
+    assert bench.stored_trace_ns("fake") is None            # no summary yet
+    h = bench.kernel_source_hash("fake")
+    summary.write_text(f"dominant_path: slab\ndominant_kernel_trace_mean_ns: 900\nkernel_source_sha256: {h}\n")
+    assert bench.stored_trace_ns("fake") is None            # another path's figure
+    summary.write_text(f"dominant_path: fake\ndominant_kernel_trace_mean_ns: 900\nkernel_source_sha256: {h}\n")
+    assert bench.stored_trace_ns("fake") == 900.0
+    fake_kernel.write_text("int f(int a) { return a; }\n")  # the code changed since
+    assert bench.stored_trace_ns("fake") is None
+
+
+def test_committed_trace_summary_matches_the_slab_sources():
+    # the committed summary names the slab kernel; its figure is used only while the sources match
+    ns = bench.stored_trace_ns("slab")
+    assert ns is None or 50e3 < ns < 200e3
