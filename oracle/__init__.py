@@ -165,9 +165,39 @@ def conv_bwd_data(dy: np.ndarray, w: np.ndarray, x_shape, stride=1, padding=0, d
     return (dx, int(macs)) if return_macs else dx
 
 
+def decode_fp16_bits(bits: np.ndarray) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) to float64, from the format's fields: sign bit 15,
+    5-bit exponent (bias 15), 10-bit fraction; exponent 0 is the subnormal range
+    (fraction * 2^-24), exponent 31 is infinity (fraction 0) or NaN.  Exact: every binary16
+    value is a binary64 value."""
+    b = bits.astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    normal = np.ldexp(1024.0 + f, (e - 25).astype(np.int32))   # (1 + f/2^10) * 2^(e-15)
+    sub = np.ldexp(f, -24)
+    special = np.where(f == 0, np.inf, np.nan)
+    return sign * np.where(e == 0, sub, np.where(e == 31, special, normal))
+
+
+def decode_bf16_bits(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) to float64: a bfloat16 is the upper half of the binary32
+    with the same sign, exponent and leading fraction bits, so the pattern shifted left by 16
+    is that binary32, which widens to binary64 exactly."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 def to_float64(t) -> np.ndarray:
-    """Exact float64 copy of a CPU or GPU fp16 / bf16 / fp32 tensor (or ndarray)."""
+    """Exact float64 copy of a CPU or GPU fp16 / bf16 / fp32 tensor (or ndarray).  torch only
+    moves the tensor to the host and hands over its raw bits; fp16 and bf16 are decoded from
+    those bits here."""
     if isinstance(t, np.ndarray):
+        if t.dtype == np.float16:
+            return decode_fp16_bits(t.view(np.uint16))
         return t.astype(np.float64)
     import torch
-    return t.detach().to("cpu").to(dtype=torch.float64).numpy()
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype in (torch.float16, torch.bfloat16):
+        bits = t.view(torch.int16).numpy().view(np.uint16)
+        return decode_fp16_bits(bits) if t.dtype == torch.float16 else decode_bf16_bits(bits)
+    return t.numpy().astype(np.float64)

@@ -256,6 +256,42 @@ def test_decode_formats_exactly():
     np.testing.assert_array_equal(oracle.to_float64(f32), [1.0 + 2.0**-23, 2.0**-149])
 
 
+def test_fp16_decode_every_pattern():
+    """All 65536 binary16 patterns against the format's definition written per class:
+    zeros, subnormals m * 2^-24, normals (1024 + m) * 2^(e - 25), infinities, NaNs; and
+    the sign symmetry."""
+    bits = np.arange(65536, dtype=np.uint16)
+    got = oracle.decode_fp16_bits(bits)
+    e, m = (bits.astype(np.int64) >> 10) & 31, bits.astype(np.int64) & 1023
+    pos = bits < 0x8000
+    assert got[0x0000] == 0.0 and got[0x0001] == 2.0**-24 and got[0x03FF] == 1023 * 2.0**-24
+    assert got[0x0400] == 2.0**-14 and got[0x3C00] == 1.0 and got[0x3C01] == 1.0 + 2.0**-10
+    assert got[0x7BFF] == 65504.0 and got[0x7C00] == np.inf and np.isnan(got[0x7C01])
+    assert np.all(np.isnan(got[(e == 31) & (m != 0)]))
+    finite = e < 31
+    assert np.all(got[finite & pos] * -1 == got[(bits | 0x8000)[finite & pos]])
+    # strictly increasing over the positive finite patterns, and each step is the spacing
+    # of the lower pattern's binade (2^-24 below 2^-14, 2^(e-25) above)
+    vals = got[:0x7C00]
+    steps = np.diff(vals)
+    expect = np.ldexp(1.0, (np.maximum(e[:0x7C00 - 1], 1) - 25).astype(np.int32))
+    np.testing.assert_array_equal(steps, expect)
+    # agreement with numpy's own binary16 on every finite pattern
+    np.testing.assert_array_equal(got[finite], bits[finite].view(np.float16).astype(np.float64))
+
+
+def test_bf16_decode_against_fp32_fields():
+    """bfloat16 patterns decode to the binary32 with the same upper 16 bits: exponent, sign
+    and 7 fraction bits, spot-checked per class (subnormal, normal, infinity, NaN)."""
+    bits = np.array([0x0000, 0x0001, 0x007F, 0x0080, 0x3F80, 0x3F81, 0x7F7F, 0x7F80, 0xFF80, 0x7FC0,
+                     0xBF80], dtype=np.uint16)
+    got = oracle.decode_bf16_bits(bits)
+    assert got[0] == 0.0 and got[1] == 2.0**-133 and got[2] == 127 * 2.0**-133
+    assert got[3] == 2.0**-126 and got[4] == 1.0 and got[5] == 1.0 + 2.0**-7
+    assert got[6] == (2 - 2.0**-7) * 2.0**127 and got[7] == np.inf and got[8] == -np.inf
+    assert np.isnan(got[9]) and got[10] == -1.0
+
+
 # --- the variants: grouped, dilated, asymmetric padding ("Convolution variants worth
 #     knowing" on the tutorial page; pads per side as in the MLX benchmark tables) -----------
 
