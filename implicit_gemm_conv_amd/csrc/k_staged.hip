@@ -486,15 +486,24 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
         const int pos = 16 * ah + rr;
         const uint32_t pbase = (uint32_t)(th * SEGB + lead + 2 * pos * p.cout + 8 * g);
         const bool pos_ok = pos < nv;
+        // the lane's 4 channels start on a 4-byte boundary of LDS (and of y)
+        // or 2 bytes past one: one aligned dword write and two 2-byte writes
+        // either way (the dword holds channels 0-1 or 1-2 of the four)
+        const bool odd = (((lead >> 1) + pos * p.cout) & 1) != 0;
 #pragma unroll
         for (int b = 0; b < NF; ++b) {
           if (all_pos && 16 * b + 16 <= p.cout) {
+            uint32_t e[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) *(T*)(smem + pbase + 2 * (16 * b + i)) = from_f32<T>(acc[a][b][i]);
-          } else {
+            for (int i = 0; i < 4; ++i) e[i] = __builtin_bit_cast(uint16_t, from_f32<T>(acc[a][b][i]));
+            char* q = smem + pbase + 32 * b;
+            *(uint32_t*)(q + (odd ? 2 : 0)) = odd ? (e[1] | (e[2] << 16)) : (e[0] | (e[1] << 16));
+            *(uint16_t*)(q + (odd ? 0 : 4)) = (uint16_t)(odd ? e[0] : e[2]);
+            *(uint16_t*)(q + 6) = (uint16_t)e[3];
+          } else if (pos_ok && 16 * b + 4 * g < p.cout) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const bool ok = pos_ok && 16 * b + 4 * g + i < p.cout;
+              const bool ok = 16 * b + 4 * g + i < p.cout;
               *(T*)(smem + (ok ? pbase + 2 * (16 * b + i) : (uint32_t)(DUMMY + 2 * lane))) = from_f32<T>(acc[a][b][i]);
             }
           }
