@@ -13,7 +13,10 @@ The JSON line also carries
                 convolutions) timed launch by launch with HIP events on the
                 launch stream (one before each launch, each launch timed to
                 the next event; timing-only events, recorded without a
-                system-scope fence), against the MI355X dense fp16 MFMA peak;
+                system-scope fence), against the MI355X dense fp16 MFMA peak.
+                Those events go into a pass of max(steps, 50) steps run
+                between the warm-up steps and the timed region, which holds
+                no event between launches;
                 The same object carries the kernel-trace figure of the committed
                 rocprofv3 summary (trace_us, trace_frac) when that summary was
                 taken on the current kernel sources;
@@ -335,30 +338,42 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Timed region: exactly `steps` steps between two synchronisations.  One HIP
-    # event goes on the launch stream before every launch (and one after the
-    # last), so each launch is timed from its own event to the next one: one
-    # event per launch instead of a pair (each event costs the stream a few us).
+    # Per-launch times, for the per-workload figures and the roofline: at
+    # least 50 steps (more samples than a short timed region gives) with one
+    # HIP event before every launch (and one after the last), each launch
+    # timed from its own event to the next one.  This pass runs after the
+    # warm-up steps and before the timed region.
     timer = HipTimer()
-    ev = [[timer.event() for _ in wls] for _ in range(args.steps)]
+    n_ev = max(args.steps, 50)
+    ev = [[timer.event() for _ in wls] for _ in range(n_ev)]
+    ev_end = timer.event()
+    torch.cuda.synchronize()
+    for s in range(n_ev):
+        step(ev[s])
+    timer.record(ev_end, stream)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly `steps` steps between two synchronisations, with one
+    # HIP event on the launch stream at each end and nothing else in between
+    # (an event recorded between launches costs the stream a few us).
     t_start = timer.event()
     t_end = timer.event()
     torch.cuda.synchronize()
     timer.record(t_start, stream)
     for s in range(args.steps):
-        step(ev[s])
+        step()
     timer.record(t_end, stream)
     torch.cuda.synchronize()
     total_ms = timer.ms(t_start, t_end)
     ms_per_step = total_ms / args.steps
 
     def launch_ms(s, i):
-        nxt = ev[s][i + 1] if i + 1 < len(wls) else (ev[s + 1][0] if s + 1 < args.steps else t_end)
+        nxt = ev[s][i + 1] if i + 1 < len(wls) else (ev[s + 1][0] if s + 1 < n_ev else ev_end)
         return timer.ms(ev[s][i], nxt)
 
     per = {}
     for i, wl in enumerate(wls):
-        times = [launch_ms(s, i) for s in range(args.steps)]
+        times = [launch_ms(s, i) for s in range(n_ev)]
         us = 1e3 * float(np.mean(times))
         per[wl.name] = {"path": kernel_key(wl), "us_mean": round(us, 3),
                         "us_min": round(1e3 * float(np.min(times)), 3),
@@ -370,7 +385,7 @@ def main():
     share = {k: sum(per[wl.name]["us_mean"] for wl, kk in zip(wls, keys) if kk == k) for k in set(keys)}
     dom_path = max(share, key=share.get)
     dom = [i for i, k in enumerate(keys) if k == dom_path]
-    dom_us = float(np.mean([1e3 * launch_ms(s, i) for s in range(args.steps) for i in dom]))
+    dom_us = float(np.mean([1e3 * launch_ms(s, i) for s in range(n_ev) for i in dom]))
     timer.close()
     dom_flops = float(np.mean([flops[i] for i in dom]))
     achieved = dom_flops / (dom_us * 1e-6) / 1e12
@@ -379,7 +394,8 @@ def main():
                  for wl in wls]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["fp16"],
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["fp16"], 4),
-                "timer": "HIP events on the launch stream, one per launch, each launch timed to the next event",
+                "timer": "HIP events on the launch stream, one per launch, each launch timed to the next event "
+                         "(a pass of max(steps, 50) steps between the warm-up and the timed region)",
                 "traffic": stored_traffic(dom_path),
                 "kernel": KERNELS.get(dom_path, (dom_path,))[0] + " (" +
                           ", ".join(wls[i].name.split("_")[0] for i in dom) + ")",
