@@ -41,9 +41,17 @@ struct RowInfo {
 // Bits t with 0 <= i0 + t*e < size set, t < k <= 16 (so every shift is < 32):
 // the taps t in [ceil(-i0 / e), floor((size - 1 - i0) / e)] of a filter whose
 // taps are e positions apart.
+// Undilated filters (e == 1, a value every workgroup shares, so the branch is
+// uniform) need no division.
 __device__ __forceinline__ uint32_t dim_mask(int i0, int k, int size, int e = 1) {
-  const int lo = i0 >= 0 ? 0 : (-i0 + e - 1) / e;
-  const int hi = i0 > size - 1 ? 0 : min(k, (size - 1 - i0) / e + 1);
+  int lo, hi;
+  if (e == 1) {
+    lo = max(0, -i0);
+    hi = min(k, size - i0);
+  } else {
+    lo = i0 >= 0 ? 0 : (-i0 + e - 1) / e;
+    hi = i0 > size - 1 ? 0 : min(k, (size - 1 - i0) / e + 1);
+  }
   if (hi <= lo) return 0u;
   return ((1u << hi) - 1u) & ~((1u << lo) - 1u);
 }
