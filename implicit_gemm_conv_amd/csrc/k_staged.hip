@@ -48,8 +48,11 @@
 // reads are interleaved one after every third MFMA of the current block (the
 // scheduler would otherwise issue them in one burst).  LDS: slab position o
 // of row r at (34 r + o) * 64 bytes, filter row kw NB + n at (kw NB + n) * 64,
-// their four 16-byte pieces XOR-swizzled by bits 2..3 of o (of the row), so
-// that 16 lanes reading 16 consecutive positions hit distinct bank groups.
+// their four 16-byte pieces XOR-swizzled by bits 1..2 of o (of the row).  A
+// 16x16x32 operand read has lanes l and l + 16 fetch other pieces of the same
+// 16 positions; measured with a read-only probe, this swizzle serves that
+// pattern at the full LDS rate (~200 B/clk per CU), where the bits 2..3
+// swizzle that suits the 32x32x16 operand of the slab kernel gets ~125.
 //
 // Epilogue: one output row of the tile (32 outputs x C_out channels when one
 // column tile covers C_out) is contiguous in y.  Each wave writes its four
@@ -111,7 +114,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // physical 16-byte piece of logical piece c at slab position o (or filter row o)
-__device__ __forceinline__ int swz(int o, int c) { return c ^ ((o >> 2) & 3); }
+__device__ __forceinline__ int swz(int o, int c) { return c ^ ((o >> 1) & 3); }
 
 template <typename T, int KW, int KH, int NB>
 __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, const T* __restrict__ x,
