@@ -18,8 +18,8 @@
 //    multiplied.  A lane whose tap falls in the padding gets an offset past
 //    the end of the buffer, and the hardware's range check returns zeros;
 //  * LDS rows hold BK channels in 16-byte chunks whose index is XORed with a
-//    function of the row, so the 16-byte fragment reads of 8 consecutive rows
-//    cover all banks;
+//    function of the row (chosen per row width and fragment size), so that
+//    the 16-byte fragment reads run at the full LDS rate;
 //  * each wave multiplies a (BM/WM) x (BN/WN) sub-tile in MF x MF blocks,
 //    v_mfma_f32_32x32x16 (MF = 32) or v_mfma_f32_16x16x32 (MF = 16), fp32
 //    accumulators.  On gfx950 one wave can keep the matrix unit busy with
@@ -53,13 +53,18 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Physical 16-byte chunk of logical chunk `lc` in LDS row `r` for rows of
-// CPR chunks: 8 consecutive rows reading the same logical chunk must land
-// on 8 different 16-byte bank groups of a 128-byte bank line.
-template <int CPR>
+// Physical 16-byte chunk of logical chunk `lc` in LDS row `r` (rows of CPR
+// chunks) for fragments of MF rows.  In a fragment read, lanes 0..MF-1 take
+// one chunk of MF consecutive rows and the next lane groups other chunks of
+// the same rows; timed with a read-only probe, these XOR patterns serve that
+// read at the full LDS rate (~190-210 B/clk per CU) where the others measured
+// reach 60-125: for 64-byte rows bits 1..2 of r with 16-row fragments, bits
+// 2..3 with 32-row ones; for 128-byte rows bits 1..3 with either.
+template <int CPR, int MF>
 __device__ __forceinline__ int swz(int r, int lc) {
-  if constexpr (CPR == 8) return lc ^ (r & 7);
-  else return lc ^ ((r >> 1) & 3);   // two 64-byte rows share a bank line
+  if constexpr (CPR == 8) return lc ^ ((r >> 1) & 7);
+  else if constexpr (MF == 32) return lc ^ ((r >> 2) & 3);
+  else return lc ^ ((r >> 1) & 3);
 }
 
 template <int MF> struct Acc;
@@ -125,11 +130,12 @@ __device__ __forceinline__ void main_tile(const ConvParams& p, const T* __restri
   const int c_grp = grp * p.cin_g;
 
   // Loader geometry: a wave's load instruction fills RPI consecutive tile
-  // rows (1 KB of LDS); lane l writes row l / CPR, physical chunk l % CPR,
-  // so it fetches the logical chunk that the swizzle puts there (its own
-  // inverse, being an XOR).
+  // rows (1 KB of LDS); lane l writes row l / CPR of them, physical chunk
+  // l % CPR, so it fetches the logical chunk that the swizzle puts there (its
+  // own inverse, being an XOR).  Load rounds are RPR >= 32 rows apart, so the
+  // row bits the swizzle reads are those of lrow in every round.
   const int lrow = wave * RPI + lane / CPR;
-  const int lchunk = swz<CPR>(lane / CPR, lane % CPR);
+  const int lchunk = swz<CPR, MF>(lrow, lane % CPR);
 
   const __amdgpu_buffer_rsrc_t xr =
       __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)x_bytes, kRawBufferFlags);
@@ -207,7 +213,7 @@ __device__ __forceinline__ void main_tile(const ConvParams& p, const T* __restri
     const char* sb = sa + BM * ROWB;
 #pragma unroll
     for (int ks = 0; ks < BK / KSUB; ++ks) {
-      const int chunk = swz<CPR>(fr, ks * LG + fg) * 16;
+      const int chunk = swz<CPR, MF>(fr, ks * LG + fg) * 16;
       V8 af[FM], bfr[FN];
 #pragma unroll
       for (int a = 0; a < FM; ++a)

@@ -39,9 +39,12 @@
 // by LDS fragment reads (one wave cannot keep enough reads in flight) and by
 // the per-lane set-up, which now splits over twice the waves.  Fragment reads
 // run one unit (a tap's k slice) ahead of the MFMAs.  LDS positions and filter
-// rows are 128 bytes; their 16-byte chunks are XOR-swizzled by bits 1..3 of
-// the slot (the position's index inside its phase sub-row, or the filter
-// row), so 16 lanes reading 16 consecutive slots hit 16 distinct bank groups.
+// rows are 128 bytes; their 16-byte chunks are XOR-swizzled: a filter row R by
+// bits 1..3 of R, a staged position by (s >> 1 & 3) ^ (s & 1) << 2 of its slot
+// s inside its phase sub-row.  Timed with a read-only probe, the position
+// swizzle serves the A reads of all three taps at the full LDS rate (~200
+// B/clk per CU; with bits 1..3 of s the kw = 2 tap, which starts one slot on,
+// got ~110).
 #include <type_traits>
 
 #include "conv_device.h"
@@ -63,6 +66,10 @@ constexpr int kCK = 64;             // input channels per chunk (one 128-byte po
 constexpr int kPosB = kCK * 2;      // bytes per staged position / filter row
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kWaves = 8;           // two per SIMD
+
+// XOR applied to the 16-byte chunk index of the staged position at slot s of
+// its phase sub-row
+__device__ __forceinline__ int pos_swz(int s) { return ((s >> 1) & 3) ^ ((s & 1) << 2); }
 
 template <int KH, int KW>
 struct PhaseGeom {
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvParams p, const 
       const int b = div_small<G::SR>(pos), slot = pos - b * G::SR;
       const int ph = slot >= G::SE ? 1 : 0;
       const int s = slot - ph * G::SE;             // index inside the phase sub-row
-      const int c = (lane & 7) ^ ((s >> 1) & 7);   // logical chunk this lane fetches
+      const int c = (lane & 7) ^ pos_swz(s);       // logical chunk this lane fetches
       const int r = 2 * b + odd, o = 2 * s + ph;   // staged row, position
       const uint32_t ok = (uint32_t)(b < R) & (uint32_t)((unsigned)(y0 + r) < (unsigned)p.h) &
                           (uint32_t)((unsigned)(x0 + o) < (unsigned)p.w);
@@ -239,7 +246,7 @@ __global__ __launch_bounds__(512, 1) void conv_phase_kernel(ConvParams p, const 
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int s = (r32 & 15) + e, ks = 2 * kp + t2;
-      a_off[e][t2] = ((2 * mb + (r32 >> 4)) * G::SR + s) * kPosB + (((2 * ks + kg) ^ ((s >> 1) & 7)) * 16);
+      a_off[e][t2] = ((2 * mb + (r32 >> 4)) * G::SR + s) * kPosB + (((2 * ks + kg) ^ pos_swz(s)) * 16);
     }
 #pragma unroll
   for (int t2 = 0; t2 < 2; ++t2)
