@@ -31,22 +31,26 @@
 // Tile: 16 output rows x 32 outputs along w (512 GEMM rows, one depth plane of
 // one image; rows past the output's end are computed on zeros and not
 // stored) x NB output channels, NB in {32, 64, 80}, so that C_out = 65 runs on
-// 80 columns.  Four waves, one per SIMD: wave v owns output rows 4v .. 4v + 3
-// of the tile (8 fragments of 16 outputs) x all NB channels, v_mfma_f32_
+// 80 columns.  Eight waves, two per SIMD: wave v owns output rows 2v, 2v + 1
+// of the tile (4 fragments of 16 outputs) x all NB channels, v_mfma_f32_
 // 16x16x32 blocks with the filter as the first operand, so a lane receives 4
-// consecutive channels of one output.  Per K block a wave reads 8 + NB/16
-// fragments (1 KB each) for 8 NB/16 MFMAs.  (Eight waves of half the rows
-// would leave 256 registers a wave, too few for the 80 accumulators, the
-// double-buffered fragments and the loads in flight.)
+// consecutive channels of one output.  Per K block a wave reads 4 + NB/16
+// fragments (1 KB each) for 4 NB/16 MFMAs.  A wave then fits in 256
+// registers (249 for the 3x3x3 instance with 80 columns; the K_h = 2, K_w = 3,
+// 80-column one spills two), and the second wave on each SIMD covers the
+// other's waits, which one wave per SIMD left exposed: against four waves of
+// four rows (one per SIMD, ~500 registers) this runs 4-21% faster on every
+// shape timed, C_in = 65 (4, 32^3) 44.4 -> 38.9 us, with identical results.
+// The kernel keeps the wave count as a parameter (4 or 8).
 //
 // Pipeline, per K step (chunk, kd, kh) of K_w blocks: the filter slice of
 // step t is fetched into registers (one of K_h sets) after the barrier that
 // ends step t - 3 and written to its LDS stage before the barrier that ends
 // step t - 1; the pieces of the next (chunk, kd) slab are fetched during the
-// steps before a slab's last and written before its closing barrier.  With
-// one wave per SIMD nothing else hides latency, so the next block's fragment
-// reads are interleaved one after every third MFMA of the current block (the
-// scheduler would otherwise issue them in one burst).  LDS: slab position o
+// steps before a slab's last and written before its closing barrier.  The
+// next block's fragment reads are interleaved one after every second MFMA of
+// the current block (every third with four waves; the scheduler would
+// otherwise issue them in one burst).  LDS: slab position o
 // of row r at (34 r + o) * 64 bytes, filter row kw NB + n at (kw NB + n) * 64,
 // their four 16-byte pieces XOR-swizzled by bits 1..2 of o (of the row).  A
 // 16x16x32 operand read has lanes l and l + 16 fetch other pieces of the same
@@ -55,7 +59,7 @@
 // swizzle that suits the 32x32x16 operand of the slab kernel gets ~125.
 //
 // Epilogue: one output row of the tile (32 outputs x C_out channels when one
-// column tile covers C_out) is contiguous in y.  Each wave writes its four
+// column tile covers C_out) is contiguous in y.  Each wave writes its
 // rows into LDS exactly as they lie in y, shifted so that 16-byte boundaries
 // of y and of LDS coincide, and stores aligned 16-byte pieces (element stores
 // for the partial pieces at either end); with several column tiles the
@@ -76,14 +80,12 @@ constexpr int kRawBufferFlags = 0x00020000;
 constexpr int kSeg = 32;                            // outputs along w per tile row
 constexpr int kRowsOut = 16;                        // output rows along h per tile
 constexpr int kSW = kSeg + 2;                       // slab positions per row (K_w <= 3)
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsWave = kRowsOut / kWaves;        // output rows per wave
-constexpr int kFA = 2 * kRowsWave;                  // A fragments per wave
 constexpr int kBM = kSeg * kRowsOut;                // 512 GEMM rows
-constexpr int kALoads = 10;                         // 16-byte slab pieces per thread: 40 wave loads of
-                                                    // 16 positions cover 18 x 34
-constexpr int kSlabBytes = kWaves * kALoads * 16 * 64;   // 40 KB a stage
+constexpr int kSlabLoads = 40;                      // wave loads of 16 positions per slab stage
+                                                    // (40 x 16 positions cover 18 x 34)
+constexpr int kSlabBytes = kSlabLoads * 16 * 64;    // 40 KB a stage
+constexpr int kRemLoads = 12;                       // wave loads of 64 positions per REM plane
+                                                    // (768 slots, 612 used)
 constexpr int kLdsBytes = 160 * 1024;
 constexpr int kMaxPackKd = 3;                       // depth taps with leftover channels
 
@@ -116,14 +118,20 @@ __device__ __forceinline__ void static_for(F&& f) {
 // physical 16-byte piece of logical piece c at slab position o (or filter row o)
 __device__ __forceinline__ int swz(int o, int c) { return c ^ ((o >> 1) & 3); }
 
-template <typename T, int KW, int KH, int NB>
-__global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, const T* __restrict__ x,
+template <typename T, int KW, int KH, int NB, int W>
+__global__ __launch_bounds__(64 * W, 1) void conv_staged_kernel(ConvParams p, const T* __restrict__ x,
                                                              const T* __restrict__ w, T* __restrict__ y,
                                                              StagedArgs sa) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef typename Vec8<T>::type V8;
   static_assert(NB % 16 == 0 && NB >= 16 && NB <= 80, "channels per tile");
   static_assert(KW >= 2 && KW <= 3 && KH >= 2 && KH <= 3, "filter extents");
+  static_assert(W == 4 || W == 8, "waves");
+  constexpr int kWaves = W;
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kRowsWave = kRowsOut / kWaves;     // output rows per wave
+  constexpr int kFA = 2 * kRowsWave;               // A fragments per wave
+  constexpr int kALoads = kSlabLoads / kWaves;     // slab pieces per thread
   constexpr int NF = NB / 16;                      // filter fragments per block
   constexpr int B_ROWS = KW * NB;                  // filter rows per step
   constexpr int B_BYTES = B_ROWS * 64;
@@ -138,10 +146,16 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
   constexpr int PK_B = F_BASE + 2 * B_BYTES;
   constexpr int PB_PER = NB * 32 / kThreads;       // filter-side entries per thread
   constexpr int REM = PK_B + NB * 32 * 4;
-  constexpr int REM_SLOTS = 3 * kThreads;          // slab positions (612 used) per kd plane
-  constexpr int REM_PER = REM_SLOTS / kThreads;    // REM loads per thread and plane
+  constexpr int REM_SLOTS = kRemLoads * 64;        // slab positions (612 used) per kd plane
+  constexpr int REM_PER = (kRemLoads + kWaves - 1) / kWaves;   // REM loads per thread and plane
+  // With eight waves the 12 wave loads of a plane leave 4 spare ones in the
+  // last round: they load nothing (out of range) into a 1 KB dummy area, so
+  // that every wave issues the same number of loads and the waits can count
+  // them.
+  constexpr bool REM_SPARE = REM_PER * kWaves > kRemLoads;
   constexpr int R_LOADS = PB_PER;                  // filter-side element loads per thread
-  constexpr int RING = REM + kMaxPackKd * REM_SLOTS * 16;
+  constexpr int REM_DUMMY = REM + kMaxPackKd * REM_SLOTS * 16;
+  constexpr int RING = REM_DUMMY + (REM_SPARE ? 1024 : 0);
   constexpr int SEGB = 64 * NB + 16;               // one output row as laid out in y, plus the lead
   constexpr int DUMMY = kRowsOut * SEGB;            // 64 dummy element slots
   constexpr int OUT = DUMMY + 128;
@@ -293,8 +307,8 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
   uint32_t r_base[REM_PER];
 #pragma unroll
   for (int i = 0; i < REM_PER; ++i) {
-    const int pos = i * kThreads + tid, r = pos / kSW, o = pos - r * kSW;
-    const bool ok = packed && r < kRowsOut + KH - 1 && o < kSeg + KW - 1 && (unsigned)(y0 + r) < (unsigned)p.h &&
+    const int wl = i * kWaves + wave, pos = wl * 64 + lane, r = pos / kSW, o = pos - r * kSW;
+    const bool ok = packed && wl < kRemLoads && r < kRowsOut + KH - 1 && o < kSeg + KW - 1 && (unsigned)(y0 + r) < (unsigned)p.h &&
                     (unsigned)(x0 + o) < (unsigned)p.w;
     r_base[i] = ok ? ubase + __umul24((unsigned)r, rowB) + __umul24((unsigned)o, posB) + rtail : kOutOfRange;
   }
@@ -302,10 +316,14 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
     const bool live = a_ic == sa.nch - 1 && ((dmask >> a_kd) & 1u) != 0u;
     const uint32_t zoff = (uint32_t)(a_kd * p.ed * p.xs_d * 2);
 #pragma unroll
-    for (int i = 0; i < REM_PER; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, (lds_ptr_t)(smem + REM + (min(a_kd, kMaxPackKd - 1) * REM_SLOTS + i * kThreads + wave * 64) * 16), 16,
-          live ? r_base[i] + zoff : kOutOfRange, 0, 0, 0);
+    for (int i = 0; i < REM_PER; ++i) {
+      const int wl = i * kWaves + wave;             // wave-uniform
+      char* dst = (!REM_SPARE || wl < kRemLoads)
+                      ? smem + REM + (min(a_kd, kMaxPackKd - 1) * REM_SLOTS + wl * 64) * 16
+                      : smem + REM_DUMMY;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, live ? r_base[i] + zoff : kOutOfRange, 0, 0,
+                                               0);
+    }
   };
   issue_rem();
   issue_a(0, kALoads);
@@ -316,7 +334,7 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
 #pragma unroll
     for (int i = i0; i < i1; ++i) {
       {
-        const int el = tid & 31, n = n0 + (tid >> 5) + 8 * i;
+        const int el = tid & 31, n = n0 + (tid >> 5) + (kThreads / 32) * i;
         const int tt = min(fast_div(el, sa.rp, sa.m_rp), p.ntaps - 1);   // entries past npe: any tap
         const uint32_t woffe = (uint32_t)((tt * p.cin + sa.cmain + el - tt * sa.rp) * 2);
         const bool ok = packed && el < sa.npe && n < p.cout;
@@ -356,10 +374,11 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
         for (int b = 0; b < NF; ++b) acc[a][b] = mfma16x16x32(bf[b], fa[a], acc[a][b]);
         fa[a] = read_a(na, nkw, a);
       }
+      constexpr int RI = kWaves == 8 ? 2 : 3;    // MFMAs per interleaved fragment read
 #pragma unroll
       for (int i = 0; i < kFA * NF; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (i % 3 == 2 && i / 3 < kFA + NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (i % RI == RI - 1 && i / RI < kFA + NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     };
 #pragma unroll
@@ -557,7 +576,7 @@ __global__ __launch_bounds__(kThreads, 1) void conv_staged_kernel(ConvParams p, 
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <typename T, int KW, int KH, int NB>
+template <typename T, int KW, int KH, int NB, int W>
 hipError_t launch_k(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
   StagedArgs sa;
   TileArgs& ta = sa.ta;
@@ -576,7 +595,7 @@ hipError_t launch_k(const ConvParams& p, const void* x, const void* w, void* y, 
   sa.npe = p.ntaps * sa.rp;
   sa.m_rp = div_magic(sa.rp);
   const int tiles_m = p.n * p.od * ta.hblocks * ta.wblocks;
-  hipLaunchKernelGGL((conv_staged_kernel<T, KW, KH, NB>), dim3(tiles_m * ta.tiles_n), dim3(kThreads), 0, s, p,
+  hipLaunchKernelGGL((conv_staged_kernel<T, KW, KH, NB, W>), dim3(tiles_m * ta.tiles_n), dim3(64 * W), 0, s, p,
                      (const T*)x, (const T*)w, (T*)y, sa);
   return hipGetLastError();
 }
@@ -585,10 +604,11 @@ hipError_t launch_k(const ConvParams& p, const void* x, const void* w, void* y, 
 // beyond, whichever of 64 and 80 pads C_out less.
 template <typename T, int KW, int KH>
 hipError_t launch_nb(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
-  if (p.cout <= 32) return launch_k<T, KW, KH, 32>(p, x, w, y, s);
-  if (p.cout <= 64) return launch_k<T, KW, KH, 64>(p, x, w, y, s);
-  if (p.cout <= 80 || (p.cout + 79) / 80 * 80 < (p.cout + 63) / 64 * 64) return launch_k<T, KW, KH, 80>(p, x, w, y, s);
-  return launch_k<T, KW, KH, 64>(p, x, w, y, s);
+  constexpr int W = 8;   // waves per workgroup, two per SIMD
+  if (p.cout <= 32) return launch_k<T, KW, KH, 32, W>(p, x, w, y, s);
+  if (p.cout <= 64) return launch_k<T, KW, KH, 64, W>(p, x, w, y, s);
+  if (p.cout <= 80 || (p.cout + 79) / 80 * 80 < (p.cout + 63) / 64 * 64) return launch_k<T, KW, KH, 80, W>(p, x, w, y, s);
+  return launch_k<T, KW, KH, 64, W>(p, x, w, y, s);
 }
 
 template <typename T, int KH>
