@@ -70,6 +70,7 @@ CASES = [
     _case("phase_fp16_2d_k2", "fp16", (2, 17, 18, 64), (72, 2, 2, 64), (2, 2), (0, 0), seed=33),
     _case("phase_fp16_k233_pad0", "fp16", (1, 7, 16, 16, 64), (64, 2, 3, 3, 64), (2, 2, 2), (0, 0, 0), seed=34),
     _case("phase_bf16_k32_o200", "bf16", (1, 4, 18, 23, 192), (200, 1, 3, 2, 192), (1, 2, 2), (0, 1, 1), seed=35),
+    _case("phase_fp16_2d_k23_o48", "fp16", (2, 15, 21, 64), (48, 2, 3, 64), (2, 2), (0, 1), seed=61),
     # C_in not a multiple of 8: 32-channel chunks plus the packed leftover block; ragged h and w
     # blocks, 80-, 64- and 32-channel tiles, two column tiles (element-wise stores), pack only
     _case("staged_bf16_c65_o65_ragged", "bf16", (1, 5, 19, 37, 65), (65, 3, 3, 3, 65), (1, 1, 1), (1, 1, 1),
