@@ -12,10 +12,14 @@
 // step of an output row is 32 consecutive input elements.  Rows of odd
 // channel counts are only 2-byte aligned: a step is fetched as 16-byte pieces
 // with unaligned buffer loads, and the columns of window positions that fall
-// in the padding (or past the run) are zeroed with branch-free masks.  Pieces
-// that would start before x or reach past the end of a tensor (only possible
-// on its first and last lines) are fetched element by element, since the
-// buffer range check drops any dword that is not wholly inside the tensor.
+// in the padding (or past the run) are zeroed with branch-free masks.  A
+// piece that would start before x or reach past the end of a tensor (only on
+// its first and last lines; the buffer range check would drop its dwords
+// whole, and a 2-byte element can share a dword with bytes past the end) is
+// loaded from the nearest 16 bytes inside the tensor and moved into place
+// with byte-align instructions when it is consumed.  (Fetching those pieces
+// element by element made the waves holding them wait for every load in
+// flight at each such step: 3-4.5 us on the C_in = 21 and fp32 layers.)
 // Grouped or w-dilated problems use shorter runs: the C_in/G channels of one
 // tap, a group's slice of one window position.
 //
@@ -71,30 +75,32 @@ __device__ __forceinline__ u4 keep_range(u4 v, int jl, int jh) {
   return r;
 }
 
-// The 16 bytes at element offset e of a tensor of `bytes` bytes, where only
-// elements j with jl <= j < jh are wanted: one unaligned 16-byte load when the
-// piece lies wholly inside the tensor, else element loads of the wanted ones.
+// The 16 bytes at element offset e of a tensor of `bytes` >= 16 bytes.  A
+// piece that starts before the tensor or runs past its end (only on its first
+// and last lines) is loaded from the nearest 16 bytes inside it instead, and
+// *shift = (piece start - load start) in bytes, -15 .. 15, tells the consumer
+// to move it into place (shift_piece) once it has arrived; 0 for a piece
+// wholly inside.  One load per piece either way and no wait at issue: the
+// consumer's wait is the pipeline's own.
 template <int EB>
-__device__ __forceinline__ u4 load_piece(__amdgpu_buffer_rsrc_t rsrc, int e, bool ok, int jl, int jh,
-                                         int bytes) {
+__device__ __forceinline__ u4 load_piece(__amdgpu_buffer_rsrc_t rsrc, int e, bool ok, int bytes, int* shift) {
   const int bo = e * EB;
-  const bool whole = ok && bo >= 0 && bo <= bytes - 16;
-  u4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, whole ? (uint32_t)bo : kOutOfRange, 0, 0);
-  if (ok && !whole) {   // first or last line of the tensor: rare, element by element
-    constexpr int EPC = 16 / EB;
+  const int c = min(max(bo, 0), bytes - 16);
+  *shift = ok ? bo - c : 0;
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc, ok ? (uint32_t)c : kOutOfRange, 0, 0);
+}
+
+// Byte j of the result is byte j + s of v (-16 < s < 16), zero where that lies
+// outside v: v placed in a zero-padded 48-byte window, four dwords taken at
+// byte 16 + s with v_alignbyte.
+__device__ __forceinline__ u4 shift_piece(u4 v, int s) {
+  const int t = 16 + s;
+  const int dw = t >> 2, b = t & 3;
+  auto z = [&](int k) -> uint32_t { return k == 4 ? v[0] : k == 5 ? v[1] : k == 6 ? v[2] : k == 7 ? v[3] : 0u; };
+  u4 r;
 #pragma unroll
-    for (int j = 0; j < EPC; ++j) {
-      const int be = bo + j * EB;
-      const bool want = j >= jl && j < jh && be >= 0 && be <= bytes - EB;
-      if constexpr (EB == 4) {
-        v[j] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, want ? (uint32_t)be : kOutOfRange, 0, 0);
-      } else {
-        const uint32_t h = __builtin_amdgcn_raw_buffer_load_b16(rsrc, want ? (uint32_t)be : kOutOfRange, 0, 0);
-        v[j >> 1] = (j & 1) ? ((v[j >> 1] & 0x0000ffffu) | (h << 16)) : ((v[j >> 1] & 0xffff0000u) | h);
-      }
-    }
-  }
-  return v;
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_alignbyte(z(dw + i + 1), z(dw + i), (uint32_t)b);
+  return r;
 }
 
 template <typename T, int BM, int BN, int DEPTH>
@@ -178,23 +184,33 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   // Loads of the step (kd, kh, k0) into register slot `slot`; steps past the
   // end load nothing.
   u4 ra[DEPTH][A_PER], rb[DEPTH][B_PER];
+  // shift_piece amounts of a slot's pieces (0 almost always), 5-bit two's
+  // complement fields: A piece i at bit 5 i, B piece j at bit 5 (A_PER + j)
+  static_assert(A_PER + B_PER <= 6, "shift fields");
+  uint32_t sh_packed[DEPTH];
   int l_kd = 0, l_kh = 0, l_kw = 0, l_k0 = 0, l_step = 0;
   int s_k0[DEPTH];   // column offset of the step in each slot (for the masks)
   auto load_step = [&](int slot) {
     const bool live = l_step < S;
     const int xo = l_kd * p.ed * p.xs_d + l_kh * p.eh * p.xs_h + l_kw * p.ew * p.xs_w + l_k0;
     const int wo = ((l_kd * p.kh + l_kh) * nkw + l_kw) * run + l_k0;
+    uint32_t packed = 0u;
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
       // a piece wholly outside the row's valid columns is not loaded (reads as zero)
       const bool ok = live && ((a_dh[i] >> l_kd) & (a_dh[i] >> (16 + l_kh)) & (a_w[i] >> l_kw) & 1u) &&
                       a_lo[i] - l_k0 < EPC && a_hi[i] - l_k0 > 0;
-      ra[slot][i] = load_piece<EB>(xr, a_e[i] + xo, ok, a_lo[i] - l_k0, a_hi[i] - l_k0, x_bytes);
+      int sh;
+      ra[slot][i] = load_piece<EB>(xr, a_e[i] + xo, ok, x_bytes, &sh);
+      packed |= ((uint32_t)sh & 31u) << (5 * i);
     }
 #pragma unroll
-    for (int j = 0; j < B_PER; ++j)
-      rb[slot][j] = load_piece<EB>(wr, b_e[j] + wo, live && b_ok[j] && b_hi[j] - l_k0 > 0, 0, b_hi[j] - l_k0,
-                                   w_bytes);
+    for (int j = 0; j < B_PER; ++j) {
+      int sh;
+      rb[slot][j] = load_piece<EB>(wr, b_e[j] + wo, live && b_ok[j] && b_hi[j] - l_k0 > 0, w_bytes, &sh);
+      packed |= ((uint32_t)sh & 31u) << (5 * (A_PER + j));
+    }
+    sh_packed[slot] = packed;
     s_k0[slot] = l_k0;
     l_k0 += kBK;
     if (l_k0 >= run) {
@@ -225,6 +241,17 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   auto run_step = [&](int step, int slot) {
     char* st = smem + (step & 1) * STAGE;
     const int k0 = s_k0[slot];
+    // pieces loaded from a clamped offset at a tensor's first or last line:
+    // moved into place now that they have arrived (a wave-uniform branch)
+    if (__builtin_amdgcn_ballot_w64(sh_packed[slot] != 0u) != 0) {
+      const uint32_t pk = sh_packed[slot];
+      // field f, sign-extended from 5 bits
+      auto field = [&](int f) { return (int)(pk << (27 - 5 * f)) >> 27; };
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) ra[slot][i] = shift_piece(ra[slot][i], field(i));
+#pragma unroll
+      for (int j = 0; j < B_PER; ++j) rb[slot][j] = shift_piece(rb[slot][j], field(A_PER + j));
+    }
     // Only a piece that a valid-column boundary cuts needs masking (pieces
     // wholly outside were not loaded); most steps of most waves have none, so
     // the masks are skipped for the whole wave then.
@@ -271,7 +298,8 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
   };
   for (int s = 0; s < S; s += DEPTH) {
 #pragma unroll
-    for (int t = 0; t < DEPTH; ++t) run_step(s + t, t);
+    for (int t = 0; t < DEPTH; ++t)
+      if (s + t < S) run_step(s + t, t);   // uniform: the last round stops at the last step
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // loads past the end
 
@@ -346,8 +374,10 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
 }  // namespace
 
 bool runs_accepts(const ConvParams& p, int dtype) {
-  (void)dtype;
-  return p.kd <= 16 && p.kh <= 16 && p.kw <= 16;
+  // pieces at a tensor's ends are loaded as the 16 bytes that end or start it
+  const int64_t eb = dtype == kF32 ? 4 : 2;
+  const bool big = p.n == 0 || ((int64_t)p.n * p.xs_n * eb >= 16 && (int64_t)p.cout * p.K * eb >= 16);
+  return big && p.kd <= 16 && p.kh <= 16 && p.kw <= 16;
 }
 
 hipError_t launch_runs(const ConvParams& p, int dtype, const void* x, const void* w, void* y,
