@@ -99,7 +99,8 @@ typedef enum {
   CONVFWD_PATH_RUNS = 7,   /* any dtype and C_in, filter <= 16 per dim, x and w of at least 16
                               bytes (the unaligned-channel tail path and fp32): the K_w * C_in
                               columns of each (kd, kh) read as one contiguous run, 16-byte
-                              unaligned pieces, MFMA */
+                              unaligned pieces, MFMA; with few tiles, 16-row tiles whose four
+                              waves split the K walk */
   CONVFWD_PATH_GROUPED = 8, /* any dtype, G > 1 with C_in/G in {1, 2, 4, 8, 16}, C_out/G <= 16 and
                               C_out * K_d*K_h*K_w * C_in/G <= 16384 (depthwise and small groups):
                               one thread per (output position, group), fp32 FMA, filter in LDS */
