@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
 // With 64-row tiles the fp32 (1,8^3,16->32) layer makes 8 workgroups (32 busy
 // SIMDs of 1024) and the C_in = 21 (4,16^3) layer one per CU, and each runs a
 // serial chain of short K steps, each a barrier and an LDS round trip apart.
-// Here a workgroup owns 16 output rows x BN columns and its four waves take
+// Here a workgroup owns 16 FM output rows x BN columns and its four waves take
 // every fourth step of the same K walk.  In a 16 x 16 MFMA fragment, lane l
 // supplies row l % 16 at the 8 columns 8 (l / 16) .. + 7 of the step (for fp32
 // as the two 4-column halves of the eight 16x16x4 products), which is exactly
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
 // fragments straight into registers, DEPTH of its wave's steps ahead, masked
 // and shifted as above, with no LDS staging and no barrier in the loop.  At
 // the end waves 1..3 hand their partial sums to wave 0 through LDS.
-template <typename T, int BN, int DEPTH>
+template <typename T, int FM, int BN, int DEPTH>
 __global__ __launch_bounds__(256) void conv_runs_ksplit_kernel(ConvParams p, const T* __restrict__ x,
                                                                const T* __restrict__ w, T* __restrict__ y,
                                                                int tiles_n, int x_bytes, int w_bytes) {
@@ -357,14 +357,14 @@ __global__ __launch_bounds__(256) void conv_runs_ksplit_kernel(ConvParams p, con
   constexpr int EPC = 16 / EB;          // elements per piece
   constexpr int PPF = 8 / EPC;          // pieces per lane fragment: 1 (16-bit), 2 (fp32)
   constexpr int FN = BN / 16;
-  constexpr int NP = (1 + FN) * PPF;    // pieces per lane per step: the A fragment, then FN B fragments
+  constexpr int NP = (FM + FN) * PPF;   // pieces per lane per step: FM A fragments, then FN B fragments
   static_assert(BN % 16 == 0 && NP <= 12, "tile");
-  __shared__ __attribute__((aligned(16))) f32x4_t red[3][FN][64];
+  __shared__ __attribute__((aligned(16))) f32x4_t red[3][FM][FN][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int m0 = (tile / tiles_n) * 16;
+  const int m0 = (tile / tiles_n) * 16 * FM;
   const int tpg = (p.cout_g + BN - 1) / BN;
   const int tn = tile % tiles_n;
   const int grp = tn / tpg;
@@ -383,16 +383,21 @@ __global__ __launch_bounds__(256) void conv_runs_ksplit_kernel(ConvParams p, con
   const int fr = lane & 15, fg = lane >> 4;
   const int c0 = 8 * fg;                // this lane's first column of a step
 
-  // A: output row m0 + fr; its run at (kd, kh, kw) = (0, 0, 0) starts at
-  // element a_e, its valid columns are [a_lo, a_hi)
-  const RowInfo ri = decode_row(p, m0 + fr);
-  const int lo_w = ri.mw ? __builtin_ctz(ri.mw) : 0;
-  const int hi_w = ri.mw ? 32 - __builtin_clz(ri.mw) : 0;
-  const int a_e = ri.base + grp * p.cin_g;
-  const int a_lo = wide ? lo_w * p.cin : 0;
-  const int a_hi = wide ? hi_w * p.cin : p.cin_g;
-  const uint32_t a_dh = ri.md | (ri.mh << 16);
-  const uint32_t a_w = wide ? 0xffffffffu : ri.mw;
+  // A fragment a: output row m0 + 16 a + fr; its run at (kd, kh, kw) =
+  // (0, 0, 0) starts at element a_e, its valid columns are [a_lo, a_hi)
+  int a_e[FM], a_lo[FM], a_hi[FM];
+  uint32_t a_dh[FM], a_w[FM];
+#pragma unroll
+  for (int a = 0; a < FM; ++a) {
+    const RowInfo ri = decode_row(p, m0 + 16 * a + fr);
+    const int lo_w = ri.mw ? __builtin_ctz(ri.mw) : 0;
+    const int hi_w = ri.mw ? 32 - __builtin_clz(ri.mw) : 0;
+    a_e[a] = ri.base + grp * p.cin_g;
+    a_lo[a] = wide ? lo_w * p.cin : 0;
+    a_hi[a] = wide ? hi_w * p.cin : p.cin_g;
+    a_dh[a] = ri.md | (ri.mh << 16);
+    a_w[a] = wide ? 0xffffffffu : ri.mw;
+  }
   // B: filter rows n0 + 16 b + fr
   int b_e[FN];
   bool b_ok[FN];
@@ -430,22 +435,26 @@ __global__ __launch_bounds__(256) void conv_runs_ksplit_kernel(ConvParams p, con
     const bool live = l_step < nst;
     const int xo = l_kd * p.ed * p.xs_d + l_kh * p.eh * p.xs_h + l_kw * p.ew * p.xs_w + l_k0;
     const int wo = ((l_kd * p.kh + l_kh) * nkw + l_kw) * run + l_k0;
-    const bool tap = ((a_dh >> l_kd) & (a_dh >> (16 + l_kh)) & (a_w >> l_kw) & 1u) != 0u;
     uint64_t packed = 0u;
 #pragma unroll
-    for (int u = 0; u < PPF; ++u) {
-      const int cc = l_k0 + c0 + u * EPC;     // run column of the piece's first element
-      const bool ok = live && tap && a_lo - cc < EPC && a_hi - cc > 0;
-      int sh;
-      rp[slot][u] = load_piece<EB>(xr, a_e + xo + c0 + u * EPC, ok, x_bytes, &sh);
-      packed |= (uint64_t)((uint32_t)sh & 31u) << (5 * u);
+    for (int a = 0; a < FM; ++a) {
+      const bool tap = ((a_dh[a] >> l_kd) & (a_dh[a] >> (16 + l_kh)) & (a_w[a] >> l_kw) & 1u) != 0u;
+#pragma unroll
+      for (int u = 0; u < PPF; ++u) {
+        const int cc = l_k0 + c0 + u * EPC;     // run column of the piece's first element
+        const bool ok = live && tap && a_lo[a] - cc < EPC && a_hi[a] - cc > 0;
+        const int k = PPF * a + u;
+        int sh;
+        rp[slot][k] = load_piece<EB>(xr, a_e[a] + xo + c0 + u * EPC, ok, x_bytes, &sh);
+        packed |= (uint64_t)((uint32_t)sh & 31u) << (5 * k);
+      }
     }
 #pragma unroll
     for (int b = 0; b < FN; ++b)
 #pragma unroll
       for (int u = 0; u < PPF; ++u) {
         const int cc = l_k0 + c0 + u * EPC;
-        const int k = PPF * (1 + b) + u;
+        const int k = PPF * (FM + b) + u;
         int sh;
         rp[slot][k] = load_piece<EB>(wr, b_e[b] + wo + c0 + u * EPC, live && b_ok[b] && run - cc > 0, w_bytes, &sh);
         packed |= (uint64_t)((uint32_t)sh & 31u) << (5 * k);
@@ -456,9 +465,11 @@ __global__ __launch_bounds__(256) void conv_runs_ksplit_kernel(ConvParams p, con
     ++l_step;
   };
 
-  f32x4_t acc[FN];
+  f32x4_t acc[FM][FN];
 #pragma unroll
-  for (int b = 0; b < FN; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < FM; ++a)
+#pragma unroll
+    for (int b = 0; b < FN; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int t = 0; t < DEPTH; ++t) load_step(t);
@@ -474,34 +485,37 @@ __global__ __launch_bounds__(256) void conv_runs_ksplit_kernel(ConvParams p, con
     // columns outside the row's valid window or past the run read as zero
     u4 pc[NP];
 #pragma unroll
-    for (int u = 0; u < PPF; ++u) {
-      const int cc = k0 + c0 + u * EPC;
-      pc[u] = keep_range<EB>(rp[slot][u], a_lo - cc, a_hi - cc);
-    }
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int u = 0; u < PPF; ++u) {
+        const int cc = k0 + c0 + u * EPC;
+        pc[PPF * a + u] = keep_range<EB>(rp[slot][PPF * a + u], a_lo[a] - cc, a_hi[a] - cc);
+      }
 #pragma unroll
     for (int b = 0; b < FN; ++b)
 #pragma unroll
       for (int u = 0; u < PPF; ++u) {
         const int cc = k0 + c0 + u * EPC;
-        pc[PPF * (1 + b) + u] = keep_range<EB>(rp[slot][PPF * (1 + b) + u], 0, run - cc);
+        pc[PPF * (FM + b) + u] = keep_range<EB>(rp[slot][PPF * (FM + b) + u], 0, run - cc);
       }
     load_step(slot);
-    F af, bf[FN];
-    if constexpr (PPF == 1) {
-      af = __builtin_bit_cast(F, pc[0]);
-#pragma unroll
-      for (int b = 0; b < FN; ++b) bf[b] = __builtin_bit_cast(F, pc[1 + b]);
-    } else {
-      af.lo = __builtin_bit_cast(f32x4_t, pc[0]);
-      af.hi = __builtin_bit_cast(f32x4_t, pc[1]);
-#pragma unroll
-      for (int b = 0; b < FN; ++b) {
-        bf[b].lo = __builtin_bit_cast(f32x4_t, pc[2 * (1 + b)]);
-        bf[b].hi = __builtin_bit_cast(f32x4_t, pc[2 * (1 + b) + 1]);
+    // fragment f from pieces PPF f .. PPF f + PPF - 1
+    auto frag = [&](int f) {
+      F v;
+      if constexpr (PPF == 1) {
+        v = __builtin_bit_cast(F, pc[f]);
+      } else {
+        v.lo = __builtin_bit_cast(f32x4_t, pc[2 * f]);
+        v.hi = __builtin_bit_cast(f32x4_t, pc[2 * f + 1]);
       }
-    }
+      return v;
+    };
 #pragma unroll
-    for (int b = 0; b < FN; ++b) acc[b] = run_mfma(bf[b], af, acc[b]);
+    for (int a = 0; a < FM; ++a) {
+      const F af = frag(a);
+#pragma unroll
+      for (int b = 0; b < FN; ++b) acc[a][b] = run_mfma(frag(FM + b), af, acc[a][b]);
+    }
   };
   for (int s0 = 0; s0 < nst; s0 += DEPTH) {
 #pragma unroll
@@ -513,49 +527,56 @@ __global__ __launch_bounds__(256) void conv_runs_ksplit_kernel(ConvParams p, con
   // partial sums of waves 1..3 to wave 0 (same lane, same fragment layout)
   if (wave > 0) {
 #pragma unroll
-    for (int b = 0; b < FN; ++b) red[wave - 1][b][lane] = acc[b];
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int b = 0; b < FN; ++b) red[wave - 1][a][b][lane] = acc[a][b];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll
-  for (int b = 0; b < FN; ++b)
+  for (int a = 0; a < FM; ++a)
 #pragma unroll
-    for (int v = 0; v < 3; ++v) acc[b] += red[v][b][lane];
+    for (int b = 0; b < FN; ++b)
+#pragma unroll
+      for (int v = 0; v < 3; ++v) acc[a][b] += red[v][a][b][lane];
 
   // lane holds D[n = 4 fg + i][m = fr] of each 16 x 16 block
   const bool vec_ok =
       (p.cout & 3) == 0 && (p.cout_g & 3) == 0 && (((uintptr_t)y & (uintptr_t)(4 * EB - 1)) == 0);
-  const int m = m0 + fr;
-  if (m >= p.M) return;
-  T* yrow = y + out_row(p, m);
 #pragma unroll
-  for (int b = 0; b < FN; ++b) {
-    const int n = n0 + b * 16 + fg * 4;
-    if (vec_ok && n + 3 < n_end) {
-      if constexpr (EB == 2) {
-        union { T h[4]; uint2 u; } pk;
+  for (int a = 0; a < FM; ++a) {
+    const int m = m0 + 16 * a + fr;
+    if (m >= p.M) continue;
+    T* yrow = y + out_row(p, m);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[b][i]);
-        *(uint2*)(yrow + n) = pk.u;
+    for (int b = 0; b < FN; ++b) {
+      const int n = n0 + b * 16 + fg * 4;
+      if (vec_ok && n + 3 < n_end) {
+        if constexpr (EB == 2) {
+          union { T h[4]; uint2 u; } pk;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pk.h[i] = from_f32<T>(acc[a][b][i]);
+          *(uint2*)(yrow + n) = pk.u;
+        } else {
+          *(f32x4_t*)(yrow + n) = acc[a][b];
+        }
       } else {
-        *(f32x4_t*)(yrow + n) = acc[b];
-      }
-    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (n + i < n_end) yrow[n + i] = from_f32<T>(acc[b][i]);
+        for (int i = 0; i < 4; ++i)
+          if (n + i < n_end) yrow[n + i] = from_f32<T>(acc[a][b][i]);
+      }
     }
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <typename T, int BN>
+template <typename T, int FM, int BN>
 hipError_t launch_ksplit(const ConvParams& p, const void* x, const void* w, void* y, hipStream_t s) {
-  const int tiles_m = (p.M + 15) / 16;
+  const int tiles_m = (p.M + 16 * FM - 1) / (16 * FM);
   const int tiles_n = p.groups * ((p.cout_g + BN - 1) / BN);
   const int xb = (int)((int64_t)p.n * p.xs_n * sizeof(T));
   const int wb = (int)((int64_t)p.cout * p.K * sizeof(T));
-  hipLaunchKernelGGL((conv_runs_ksplit_kernel<T, BN, 4>), dim3(tiles_m * tiles_n), dim3(256), 0, s, p,
+  hipLaunchKernelGGL((conv_runs_ksplit_kernel<T, FM, BN, 4>), dim3(tiles_m * tiles_n), dim3(256), 0, s, p,
                      (const T*)x, (const T*)w, (T*)y, tiles_n, xb, wb);
   return hipGetLastError();
 }
@@ -588,11 +609,13 @@ hipError_t launch_bn(const ConvParams& p, const void* x, const void* w, void* y,
   return launch_cfg<T, BM, 128>(p, x, w, y, s);
 }
 
-// Steps of the K walk (32 columns each) and the 64-row tile count: few tiles
-// (fewer than half the CUs) and at least two steps per wave take the K walk
-// split over the waves, with column tiles of 32 or 64.  (fp32 (1,8^3,16->32),
-// 8 tiles: 17.2 -> 8.9 us.  C_in = 21 (4,16^3), 256 tiles, already fills the
-// chip and ran 4% slower split, every wave fetching the filter.)
+// Steps of the K walk (32 columns each) and the 64-row tile count: with fewer
+// 64-row tiles than two per CU and at least two steps per wave, the K walk is
+// split over the waves, with column tiles of 32 or 64: 16-row tiles under half
+// a tile per CU (fp32 (1,8^3,16->32), 8 tiles: 17.2 -> 8.9 us), else 32-row
+// tiles, whose filter fragments each serve two row fragments (C_in = 21
+// (4,16^3), 256 tiles: 14.9 -> 13.3 us; with 16-row tiles every wave fetched
+// the filter for 16 rows and it ran 4% slower than the 64-row kernel).
 int runs_steps(const ConvParams& p) {
   const bool wide = p.groups == 1 && p.ew == 1;
   const int run = wide ? p.kw * p.cin : p.cin_g;
@@ -605,7 +628,9 @@ hipError_t launch_typed(const ConvParams& p, const void* x, const void* w, void*
     const int bn = p.cout_g <= 32 ? 32 : 64;
     const int64_t tiles64 = (int64_t)(p.M + 63) / 64 * p.groups * ((p.cout_g + bn - 1) / bn);
     if (2 * tiles64 < device_cus())
-      return bn == 32 ? launch_ksplit<T, 32>(p, x, w, y, s) : launch_ksplit<T, 64>(p, x, w, y, s);
+      return bn == 32 ? launch_ksplit<T, 1, 32>(p, x, w, y, s) : launch_ksplit<T, 1, 64>(p, x, w, y, s);
+    if (tiles64 < 2 * device_cus())
+      return bn == 32 ? launch_ksplit<T, 2, 32>(p, x, w, y, s) : launch_ksplit<T, 2, 64>(p, x, w, y, s);
   }
   if constexpr (sizeof(T) == 2) {
     if ((p.M + 127) / 128 >= 512) return launch_bn<T, 128>(p, x, w, y, s);
