@@ -145,6 +145,32 @@ def test_auto_path_is_deterministic(wl):
                        y2.view(torch.uint8) if y2.dtype != torch.float32 else y2.view(torch.int32))
 
 
+# The runs path picks its tile by the number of 64-row tiles: under half a tile
+# per CU, 16-row tiles whose four waves split the K walk; under two per CU, the
+# same with 32-row tiles; else 64-row tiles with the steps staged through LDS.
+# On a 256-CU MI355X these shapes take each variant (M = 1785 and 512: 16 rows;
+# 16384: 32 rows; 32768: 64 rows), with ragged row and column tails, 32- and
+# 64-column tiles, bf16 with C_in = 21 (2-byte aligned rows) and fp32.
+RUNS_TILE_CASES = [
+    _case("runs_bf16_c21_m1785", "bf16", (1, 7, 15, 17, 21), (21, 3, 3, 3, 21), (1, 1, 1), (1, 1, 1), seed=62),
+    _case("runs_fp32_c16_o40_m512", "fp32", (1, 8, 8, 8, 16), (40, 3, 3, 3, 16), (1, 1, 1), (1, 1, 1), seed=63),
+    _case("runs_bf16_c21_o50_m16384", "bf16", (2, 8, 32, 32, 21), (50, 3, 3, 3, 21), (1, 1, 1), (1, 1, 1), seed=64),
+    _case("runs_bf16_c21_m32768", "bf16", (2, 16, 32, 32, 21), (21, 3, 3, 3, 21), (1, 1, 1), (1, 1, 1), seed=65),
+]
+
+
+@pytest.mark.parametrize("wl", RUNS_TILE_CASES, ids=[c.name for c in RUNS_TILE_CASES])
+def test_runs_tile_variants(wl):
+    """Each runs-path tile variant against the oracle on every output element, and repeated
+    launches bit-identical (the split K walk adds its partial sums in a fixed order)."""
+    print(f"[runs] {wl.name}", flush=True)
+    x, w, y = _run(wl, "runs")
+    _, _, y2 = _run(wl, "runs", x=x, w=w)
+    ref = oracle.conv_fwd(oracle.to_float64(x), oracle.to_float64(w), wl.stride, wl.padding)
+    assert_parity(oracle.to_float64(y), ref, wl.dtype, wl.name)
+    assert torch.equal(y, y2)
+
+
 @pytest.mark.parametrize("name", sorted(WORKLOADS))
 def test_parity_full_size(name):
     """Full-size workloads on the auto path (the launch the bench times), every output element
