@@ -24,7 +24,8 @@ The JSON line also carries
                 share of one step's output rows (--cpu-fraction, default the
                 whole step: every output row of the three convolutions).
 
-``--sweep`` instead times every workload shape on its own (10 warm-ups, then
+``--sweep`` instead times every workload shape on its own (warm-up launches in
+rounds of 10 until 50 ms have passed, then
 ``--launches`` launches each between two HIP events on the launch stream;
 median and min), once with resident buffers and once "cold", rotating enough
 (x, y) buffer sets (> 512 MB) that the 256 MB MALL cannot hold them; one JSON
@@ -267,13 +268,23 @@ def sweep(launches, names=None, tune=False):
             timer.close()
             return t
 
-        timed([(x, y)] * 10)
+        # warm-up: at least 10 launches and 50 ms, so that every shape is timed at the clocks
+        # the GPU settles to under load (a shape timed right after a light one otherwise
+        # runs its first milliseconds slower)
+        t0 = time.perf_counter()
+        n_warm = 0
+        while True:
+            timed([(x, y)] * 10)
+            n_warm += 10
+            if time.perf_counter() - t0 >= 0.05:
+                break
         warm = timed([(x, y)] * launches)
         cold = timed([(xs[i % sets], ys[i % sets]) for i in range(launches)])
         peak = PEAK_TFLOPS[wl.dtype]
         rec = {"workload": name, "path": "bwd_data" if bwd else kernel_key(wl), "dtype": wl.dtype,
                "gemm_mnk": [m, n, k],
-               "gflop": round(flops / 1e9, 4), "alg_mb": round(alg_bytes / 1e6, 3), "launches": launches}
+               "gflop": round(flops / 1e9, 4), "alg_mb": round(alg_bytes / 1e6, 3), "launches": launches,
+               "warmup_launches": n_warm}
         for tag, t in (("warm", warm), ("cold", cold)):
             med = float(np.median(t))
             rec[tag] = {"us_median": round(med, 2), "us_min": round(float(t.min()), 2),
