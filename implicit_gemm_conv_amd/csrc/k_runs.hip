@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void conv_runs_kernel(ConvParams p, const T
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// ---- the K walk split over the waves: 16-row tiles for problems with few tiles ----
+// ---- the K walk split over the waves: 16- or 32-row tiles for problems with few tiles ----
 // With 64-row tiles the fp32 (1,8^3,16->32) layer makes 8 workgroups (32 busy
 // SIMDs of 1024) and the C_in = 21 (4,16^3) layer one per CU, and each runs a
 // serial chain of short K steps, each a barrier and an LDS round trip apart.
